@@ -20,8 +20,8 @@ PW_STATUS_ROUTER_RANGE = 1
 STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "PW_E_UNBOUND",
                 5: "PW_E_ALIGN", 6: "PW_E_RANGE", 7: "PW_E_STATE", 8: "PW_E_NOMEM", 9: "PW_E_HIP"}
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
-            "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_layer_set_profiling",
-            "pw_layer_get_profile", "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant"]
+            "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
+            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant"]
 
 
 class PwError(RuntimeError):
@@ -58,8 +58,7 @@ def _load():
         "pw_page_table_bind": ([P, i32, i32, P, i32, P, i32], st),
         "pw_moe_forward": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_layer_status": ([P, P, ctypes.POINTER(u32)], st),
-        "pw_layer_set_profiling": ([P, i32], st),
-        "pw_layer_get_profile": ([P, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)], st),
+        "pw_moe_replay": ([P, i32, P], st),
         "pw_layer_last_bytes": ([P, P, ctypes.POINTER(ctypes.c_double)], st),
         "pw_debug_unpack": ([P, i32, i32, i32, P, P], st),
         "pw_debug_dequant": ([P, i32, P, i32, i32, P, P], st),
@@ -122,15 +121,8 @@ def pw_layer_status(layer: int, stream: int = 0) -> int:
     return flags.value
 
 
-def pw_layer_set_profiling(layer: int, enable: bool) -> None:
-    _check(lib.pw_layer_set_profiling(layer, 1 if enable else 0))
-
-
-def pw_layer_get_profile(layer: int):
-    n = ctypes.c_int32(0)
-    ms = (ctypes.c_float * 4)()
-    _check(lib.pw_layer_get_profile(layer, ctypes.byref(n), ms))
-    return n.value, list(ms)
+def pw_moe_replay(layer: int, phase: int, stream: int = 0) -> None:
+    _check(lib.pw_moe_replay(layer, phase, stream or None))
 
 
 def pw_layer_last_bytes(layer: int, stream: int = 0):

@@ -44,7 +44,6 @@ pw_status hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kStageSlots = 4;
-constexpr int kProfEvents = 5;
 
 struct Page {
     const void* planes[8] = {};
@@ -86,6 +85,7 @@ struct pw_layer_s {
     char* d_ws = nullptr;
     pw::Workspace ws{};
     int f_max = 0;
+    int n_cu = 256;
 
     // pinned staging ring for table uploads
     DevBlock* h_stage[kStageSlots] = {};
@@ -93,13 +93,15 @@ struct pw_layer_s {
     bool stage_used[kStageSlots] = {};
     int stage_i = 0;
 
-    // profiling
-    bool prof = false;
-    std::vector<std::array<hipEvent_t, kProfEvents>> ev_pool;
-    size_t ev_used = 0;
-    int n_prof = 0;
-
+    // launch record of the last forward (for pw_layer_last_bytes and pw_moe_replay)
     int last_T = 0;
+    pw::RouteParams rp{};
+    pw::BucketParams bp{};
+    pw::GemmParams gp_gu{}, gp_dn{};
+    int lds_gu = 0, lds_dn = 0;
+    const uint16_t* res_x = nullptr;
+    const float* res_y = nullptr;
+    uint16_t* res_out = nullptr;
 };
 
 namespace {
@@ -138,18 +140,21 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t act_rows = (size_t)T * k + (size_t)T * has_shared;
     auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
     size_t off = 0;
-    const size_t o_logits = off; off += al(sizeof(int64_t) * (size_t)T * E);
     const size_t o_ids = off;    off += al(sizeof(int32_t) * (size_t)T * k);
     const size_t o_w = off;      off += al(sizeof(float) * (size_t)T * k);
     const size_t o_cnt = off;    off += al(sizeof(int32_t) * (size_t)E);
     const size_t o_off = off;    off += al(sizeof(int32_t) * ((size_t)E + 1));
     const size_t o_srt = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
     const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
-    const size_t o_tc = off;     off += al(sizeof(uint32_t) * (size_t)T);
-    const size_t o_gc = off;     off += al(sizeof(uint32_t));
     const size_t o_st = off;     off += al(sizeof(uint32_t));
+    const size_t o_sc = off;     off += al(sizeof(uint32_t) * 2 * pw::N_LISTS);
     hipError_t e;
+    int cus = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess)
+        return hip_fail(e, "device attribute");
+    L->n_cu = cus > 0 ? cus : 256;
     if ((e = hipMalloc((void**)&L->d_ws, off)) != hipSuccess) {
         L->d_ws = nullptr;
         return fail(PW_E_NOMEM, "workspace (%zu bytes): %s", off, hipGetErrorString(e));
@@ -161,17 +166,16 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         return fail(PW_E_NOMEM, "page table: %s", hipGetErrorString(e));
     }
     char* b = L->d_ws;
-    L->ws.logits = (int64_t*)(b + o_logits);
     L->ws.ids = (int32_t*)(b + o_ids);
     L->ws.w = (float*)(b + o_w);
     L->ws.counts = (int32_t*)(b + o_cnt);
     L->ws.offsets = (int32_t*)(b + o_off);
     L->ws.sorted = (int32_t*)(b + o_srt);
+    L->ws.prefix = (int32_t*)(b + o_pre);
     L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
-    L->ws.tok_cnt = (uint32_t*)(b + o_tc);
-    L->ws.glob_cnt = (uint32_t*)(b + o_gc);
     L->ws.status = (uint32_t*)(b + o_st);
+    L->ws.sched = (uint32_t*)(b + o_sc);
     for (int i = 0; i < kStageSlots; ++i) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
             hipSuccess) {
@@ -181,7 +185,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess)
             return hip_fail(e, "hipEventCreate");
     }
-    if ((e = pw::launch_init_ws(L->ws, T, s)) != hipSuccess) return hip_fail(e, "init workspace");
+    if ((e = pw::launch_init_ws(L->ws, s)) != hipSuccess) return hip_fail(e, "init workspace");
     L->dev_ready = true;
     return PW_OK;
 }
@@ -198,7 +202,8 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
         DevBlock& db = h[i];
         std::memset(&db, 0, sizeof db);
         db.bits = L->bits[i];
-        for (int p = 0; p < db.bits; ++p) db.planes[p] = (uint64_t)(uintptr_t)pg.planes[p];
+        // plane p goes to slot p + 8 - b, so slot s always carries bit 7 - s of the index
+        for (int p = 0; p < db.bits; ++p) db.planes[p + 8 - db.bits] = (uint64_t)(uintptr_t)pg.planes[p];
         db.lut = (uint64_t)(uintptr_t)pg.lut;
     }
     if ((e = hipMemcpyAsync(L->d_blocks, h, sizeof(DevBlock) * n_blocks(L), hipMemcpyHostToDevice, s)) !=
@@ -211,28 +216,51 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
     return PW_OK;
 }
 
-pw_status prof_event(pw_layer_s* L, int which, hipStream_t s) {
-    if (!L->prof) return PW_OK;
-    hipError_t e;
-    if (which == 0) {
-        if (L->ev_used == L->ev_pool.size()) {
-            std::array<hipEvent_t, kProfEvents> ev{};
-            for (auto& x : ev)
-                if ((e = hipEventCreate(&x)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-            L->ev_pool.push_back(ev);
-        }
-        ++L->ev_used;
-    }
-    if ((e = hipEventRecord(L->ev_pool[L->ev_used - 1][which], s)) != hipSuccess)
-        return hip_fail(e, "hipEventRecord");
-    return PW_OK;
-}
-
 int plan_bmax(const pw_layer_s* L, int lin_lo, int lin_hi) {
     int bm = 1;
     for (int e = 0; e < L->n_total; ++e)
         for (int l = lin_lo; l <= lin_hi; ++l) bm = std::max(bm, (int)L->bits[e * 3 + l]);
     return bm;
+}
+
+
+// Enqueues the kernels of one phase of the forward recorded in L:
+// 0 routing (router + bucket sort), 1 gate_up + SwiGLU, 2 down + accumulation,
+// 3 residual hand-off.
+pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
+    const int T = L->last_T;
+    const int wg_small = 2 * L->n_cu, wg_large = L->n_cu;   // resident work-groups per launch
+    hipError_t e = hipSuccess;
+    switch (phase) {
+        case 0:
+            if ((e = pw::launch_route(L->rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
+            if ((e = pw::launch_bucket(L->bp, s)) != hipSuccess) return hip_fail(e, "bucket kernel");
+            break;
+        case 1:
+        case 2: {
+            pw::GemmParams gp = phase == 1 ? L->gp_gu : L->gp_dn;
+            const int lds = phase == 1 ? L->lds_gu : L->lds_dn;
+            const int mode = phase - 1;
+            gp.list = mode == 0 ? pw::LIST_GU_SMALL : pw::LIST_DN_SMALL;
+            if ((e = pw::launch_gemm(mode, 32, gp, lds, wg_small, s)) != hipSuccess)
+                return hip_fail(e, mode == 0 ? "gate_up kernel" : "down kernel");
+            if (T > 32) {
+                gp.list = mode == 0 ? pw::LIST_GU_LARGE : pw::LIST_DN_LARGE;
+                if ((e = pw::launch_gemm(mode, 128, gp, lds, wg_large, s)) != hipSuccess)
+                    return hip_fail(e, mode == 0 ? "gate_up kernel (large)" : "down kernel (large)");
+            }
+            break;
+        }
+        case 3:
+            if (L->res_out &&
+                (e = pw::launch_residual(L->res_x, L->res_y, L->res_out, (long)T * L->desc.d_model, s)) !=
+                    hipSuccess)
+                return hip_fail(e, "residual kernel");
+            break;
+        default:
+            return fail(PW_E_ARG, "phase %d not in 0..3", phase);
+    }
+    return PW_OK;
 }
 
 }  // namespace
@@ -249,8 +277,9 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     if (D.abi_version != PW_ABI_VERSION)
         return fail(PW_E_ARG, "abi_version %d, library is %d", D.abi_version, PW_ABI_VERSION);
     if (D.flags != 0) return fail(PW_E_ARG, "flags must be 0");
-    if (D.d_model <= 0 || D.d_model % 128)
-        return fail(PW_E_SHAPE, "d_model %d: must be a positive multiple of 128", D.d_model);
+    if (D.d_model <= 0 || D.d_model % 128 || D.d_model > pw::kMaxModel)
+        return fail(PW_E_SHAPE, "d_model %d: must be a positive multiple of 128, at most %d", D.d_model,
+                    pw::kMaxModel);
     if (D.n_experts < 1 || D.n_experts > PW_MAX_EXPERTS)
         return fail(PW_E_SHAPE, "n_experts %d: must be in 1..%d", D.n_experts, PW_MAX_EXPERTS);
     if (D.d_ffn <= 0 || D.d_ffn % 128)
@@ -261,6 +290,11 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
         return fail(PW_E_SHAPE, "top_k %d: must be in 1..min(n_experts, %d)", D.top_k, PW_MAX_TOP_K);
     if (D.max_tokens < 1 || D.max_tokens > 65536)
         return fail(PW_E_SHAPE, "max_tokens %d: must be in 1..65536", D.max_tokens);
+    {
+        const double act = ((double)D.max_tokens * (D.top_k + 1)) * std::max(D.d_ffn, D.d_ffn_shared);
+        if (act >= 2147483648.0)
+            return fail(PW_E_SHAPE, "max_tokens * (top_k + 1) * max(d_ffn, d_ffn_shared) must stay below 2^31");
+    }
     pw_layer_s* L = new (std::nothrow) pw_layer_s();
     if (!L) return fail(PW_E_NOMEM, "pw_layer_create: out of host memory");
     L->desc = D;
@@ -276,14 +310,12 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
 pw_status pw_layer_destroy(pw_layer L) {
     g_err.clear();
     if (!L) return PW_OK;
-    if (L->dev_ready || L->d_ws || L->d_blocks || L->prof || !L->ev_pool.empty()) {
+    if (L->dev_ready || L->d_ws || L->d_blocks) {
         DeviceGuard g(L->device);
         for (int i = 0; i < kStageSlots; ++i) {
             if (L->stage_ev[i]) (void)hipEventDestroy(L->stage_ev[i]);
             if (L->h_stage[i]) (void)hipHostFree(L->h_stage[i]);
         }
-        for (auto& ev : L->ev_pool)
-            for (auto& x : ev) (void)hipEventDestroy(x);
         if (L->d_ws) (void)hipFree(L->d_ws);
         if (L->d_blocks) (void)hipFree(L->d_blocks);
     }
@@ -357,10 +389,11 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     if ((st = upload_tables(L, s)) != PW_OK) return st;
 
     const int E = D.n_experts, k = D.top_k, d = D.d_model;
-    hipError_t e;
-    if ((st = prof_event(L, 0, s)) != PW_OK) return st;
+    const int has_shared = D.d_ffn_shared > 0;
+    L->last_T = T;
 
-    pw::RouteParams rp{};
+    pw::RouteParams& rp = L->rp;
+    rp = pw::RouteParams{};
     rp.x = (const uint16_t*)x;
     rp.wr = (const uint16_t*)router_w;
     rp.bias = (const uint16_t*)router_b;
@@ -368,20 +401,27 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     rp.d = d;
     rp.E = E;
     rp.k = k;
-    rp.epb = 8;
-    rp.n_eg = (E + rp.epb - 1) / rp.epb;
     rp.ws = L->ws;
     rp.y = y;
+    pw::BucketParams& bp = L->bp;
+    bp = pw::BucketParams{};
+    bp.T = T;
+    bp.E = E;
+    bp.k = k;
+    bp.has_shared = has_shared;
+    bp.tiles_gu_r = D.d_ffn / 64;
+    bp.tiles_gu_s = D.d_ffn_shared / 64;
+    bp.tiles_dn = d / 128;
+    bp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
+    bp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
+    bp.ws = L->ws;
     if (route) {
         rp.o_ids = route->topk_ids;
         rp.o_w = route->topk_w;
-        rp.o_counts = route->expert_count;
-        rp.o_offsets = route->expert_offset;
-        rp.o_sorted = route->sorted_assign;
+        bp.o_counts = route->expert_count;
+        bp.o_offsets = route->expert_offset;
+        bp.o_sorted = route->sorted_assign;
     }
-    if ((e = pw::launch_route(rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
-    if ((st = prof_event(L, 1, s)) != PW_OK) return st;
-
     pw::GemmParams gp{};
     gp.blocks = L->d_blocks;
     gp.E = E;
@@ -390,59 +430,49 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     gp.d = d;
     gp.F = D.d_ffn;
     gp.Fs = D.d_ffn_shared;
+    gp.has_shared = has_shared;
     gp.ws = L->ws;
     gp.ld_act = L->f_max;
     gp.shared_base = D.max_tokens * k;
     gp.y = y;
-    // gate_up + SwiGLU: 32-row tiles of F
-    {
-        const int bm = plan_bmax(L, PW_GATE, PW_UP);
-        const int lds = pw::gemm_lds_bytes(bm);
-        gp.lds_stripe = lds - pw::kTokInfoBytes;
-        gp.tiles_r = D.d_ffn / 32;
-        gp.tiles_s = D.d_ffn_shared / 32;
-        gp.n_work = E * gp.tiles_r + gp.tiles_s;
-        gp.min_count = 1;
-        gp.max_count = 32;
-        if ((e = pw::launch_gemm(0, 32, gp, lds, 1, s)) != hipSuccess) return hip_fail(e, "gate_up kernel");
-        if (T > 32) {
-            gp.min_count = 33;
-            gp.max_count = 1 << 30;
-            if ((e = pw::launch_gemm(0, 128, gp, lds, (T + 127) / 128, s)) != hipSuccess)
-                return hip_fail(e, "gate_up kernel (large)");
-        }
-    }
-    if ((st = prof_event(L, 2, s)) != PW_OK) return st;
-    // down + weighted scatter-accumulate: 64-row tiles of d
-    {
-        const int bm = plan_bmax(L, PW_DOWN, PW_DOWN);
-        const int lds = pw::gemm_lds_bytes(bm);
-        gp.lds_stripe = lds - pw::kTokInfoBytes;
-        gp.tiles_r = d / 64;
-        gp.tiles_s = D.d_ffn_shared > 0 ? d / 64 : 0;
-        gp.n_work = E * gp.tiles_r + gp.tiles_s;
-        gp.min_count = 1;
-        gp.max_count = 32;
-        if ((e = pw::launch_gemm(1, 32, gp, lds, 1, s)) != hipSuccess) return hip_fail(e, "down kernel");
-        if (T > 32) {
-            gp.min_count = 33;
-            gp.max_count = 1 << 30;
-            if ((e = pw::launch_gemm(1, 128, gp, lds, (T + 127) / 128, s)) != hipSuccess)
-                return hip_fail(e, "down kernel (large)");
-        }
-    }
-    if ((st = prof_event(L, 3, s)) != PW_OK) return st;
-    if (x_next) {
-        if ((e = pw::launch_residual((const uint16_t*)x, y, (uint16_t*)x_next, (long)T * d, s)) != hipSuccess)
-            return hip_fail(e, "residual kernel");
-    }
-    if ((st = prof_event(L, 4, s)) != PW_OK) return st;
-    if (L->prof) ++L->n_prof;
-    L->last_T = T;
+    // gate_up + SwiGLU: items of 64 rows of F
+    L->lds_gu = pw::gemm_lds_bytes(plan_bmax(L, PW_GATE, PW_UP));
+    L->gp_gu = gp;
+    L->gp_gu.lds_stripe = L->lds_gu - pw::kTokInfoBytes - (PW_MAX_EXPERTS + 2) * 4 - 16;
+    L->gp_gu.tiles_r = D.d_ffn / 64;
+    L->gp_gu.tiles_s = D.d_ffn_shared / 64;
+    L->gp_gu.pieces_r = L->gp_gu.pieces_s = 1;
+    L->gp_gu.b_bytes = (uint32_t)((size_t)D.max_tokens * d * 2);
+    // down + weighted scatter-accumulate: items of 128 rows of d
+    L->lds_dn = pw::gemm_lds_bytes(plan_bmax(L, PW_DOWN, PW_DOWN));
+    L->gp_dn = gp;
+    L->gp_dn.lds_stripe = L->lds_dn - pw::kTokInfoBytes - (PW_MAX_EXPERTS + 2) * 4 - 16;
+    L->gp_dn.tiles_r = d / 128;
+    L->gp_dn.tiles_s = has_shared ? d / 128 : 0;
+    L->gp_dn.pieces_r = bp.pieces_dn_r;
+    L->gp_dn.pieces_s = has_shared ? bp.pieces_dn_s : 1;
+    L->gp_dn.b_bytes = (uint32_t)(((size_t)D.max_tokens * k + (size_t)D.max_tokens * has_shared) * L->f_max * 2);
+    L->res_x = (const uint16_t*)x;
+    L->res_y = y;
+    L->res_out = (uint16_t*)x_next;
+
+    for (int phase = 0; phase < 4; ++phase)
+        if ((st = launch_phase(L, phase, s)) != PW_OK) return st;
     if (getenv("PW_DEBUG_SYNC")) {
-        if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "pw_moe_forward (debug sync)");
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "pw_moe_forward (debug sync)");
     }
     return PW_OK;
+}
+
+pw_status pw_moe_replay(pw_layer L, int32_t phase, void* stream) {
+    g_err.clear();
+    if (!L) return fail(PW_E_ARG, "pw_moe_replay: null layer");
+    if (!L->dev_ready || L->last_T == 0) return fail(PW_E_STATE, "pw_moe_replay: no forward has run");
+    if (phase < 0 || phase > 3) return fail(PW_E_ARG, "phase %d not in 0..3", phase);
+    DeviceGuard guard(L->device);
+    if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
+    return launch_phase(L, phase, (hipStream_t)stream);
 }
 
 pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
@@ -464,34 +494,6 @@ pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
     }
     *flags = v;
     if (v) return fail(PW_E_STATE, "device status flags 0x%x (router range)", v);
-    return PW_OK;
-}
-
-pw_status pw_layer_set_profiling(pw_layer L, int32_t enable) {
-    g_err.clear();
-    if (!L) return fail(PW_E_ARG, "pw_layer_set_profiling: null layer");
-    L->prof = enable != 0;
-    L->ev_used = 0;
-    L->n_prof = 0;
-    return PW_OK;
-}
-
-pw_status pw_layer_get_profile(pw_layer L, int32_t* n_calls, float* ms) {
-    g_err.clear();
-    if (!L || !n_calls || !ms) return fail(PW_E_ARG, "pw_layer_get_profile: null argument");
-    DeviceGuard guard(L->device);
-    for (int i = 0; i < 4; ++i) ms[i] = 0.0f;
-    hipError_t e;
-    for (size_t c = 0; c < L->ev_used; ++c) {
-        auto& ev = L->ev_pool[c];
-        if ((e = hipEventSynchronize(ev[kProfEvents - 1])) != hipSuccess) return hip_fail(e, "profile sync");
-        for (int i = 0; i < 4; ++i) {
-            float t = 0.0f;
-            if ((e = hipEventElapsedTime(&t, ev[i], ev[i + 1])) != hipSuccess) return hip_fail(e, "elapsed");
-            ms[i] += t;
-        }
-    }
-    *n_calls = (int32_t)L->ev_used;
     return PW_OK;
 }
 
@@ -537,7 +539,7 @@ pw_status pw_debug_unpack(const void* const* planes, int32_t b, int32_t R, int32
     uint64_t p8[8] = {};
     for (int p = 0; p < b; ++p) {
         if (!planes[p] || !aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d null or misaligned", p);
-        p8[p] = (uint64_t)(uintptr_t)planes[p];
+        p8[p + 8 - b] = (uint64_t)(uintptr_t)planes[p];
     }
     hipError_t e = pw::launch_debug(p8, b, nullptr, R, K, idx_out, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? PW_OK : hip_fail(e, "debug kernel");
@@ -553,7 +555,7 @@ pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut
     uint64_t p8[8] = {};
     for (int p = 0; p < b; ++p) {
         if (!planes[p] || !aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d null or misaligned", p);
-        p8[p] = (uint64_t)(uintptr_t)planes[p];
+        p8[p + 8 - b] = (uint64_t)(uintptr_t)planes[p];
     }
     hipError_t e = pw::launch_debug(p8, b, (const uint16_t*)lut, R, K, nullptr, (uint16_t*)w_out,
                                     (hipStream_t)stream);

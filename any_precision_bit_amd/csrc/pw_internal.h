@@ -10,26 +10,31 @@ namespace pw {
 // One entry of the device page table: the pages of one (expert, linear) block
 // at its planned bitwidth. 80 bytes, read with scalar loads by the kernels.
 struct DevBlock {
-    uint64_t planes[8];  // device addresses of planes 0..bits-1 (rest 0)
+    uint64_t planes[8];  // slot s: device address of plane s - (8 - bits); slots below 8 - bits are 0
     uint64_t lut;        // device address of LUT_bits, R * 2^bits fp16
     int32_t bits;        // 1..8
     int32_t pad;
 };
 static_assert(sizeof(DevBlock) == 80, "DevBlock layout");
 
+// Work lists of the gemm kernels: for list position p (p = 0 is the shared
+// expert when there is one, then routed experts 0..E-1), items
+// [prefix[p], prefix[p+1]) belong to that expert; item i of an expert is
+// (row tile i % tiles, token group i / tiles).
+enum { LIST_GU_SMALL = 0, LIST_GU_LARGE = 1, LIST_DN_SMALL = 2, LIST_DN_LARGE = 3, N_LISTS = 4 };
+
 // Workspace carved out of one device allocation per layer.
 struct Workspace {
-    int64_t* logits;     // [max_T][E]   exact logits, units of 2^-48
     int32_t* ids;        // [max_T][k]
     float* w;            // [max_T][k]
     int32_t* counts;     // [E]
     int32_t* offsets;    // [E+1]
     int32_t* sorted;     // [max_T*k]    assignment t*k+j, grouped by expert
+    int32_t* prefix;     // [N_LISTS][E+2]
     uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
-    uint32_t* tok_cnt;   // [max_T]      per-token arrival counters (last-block pattern)
-    uint32_t* glob_cnt;  // [1]          per-call arrival counter
     uint32_t* status;    // [1]          PW_STATUS_* bits
+    uint32_t* sched;     // [N_LISTS][2] work-item counter and exit counter per gemm list
 };
 
 struct RouteParams {
@@ -37,43 +42,51 @@ struct RouteParams {
     const uint16_t* wr;
     const uint16_t* bias;  // may be null
     int T, d, E, k;
-    int n_eg;              // expert groups (grid.x)
-    int epb;               // experts per group
     Workspace ws;
     float* y;              // zeroed here
-    // optional caller copies of the routing outputs
-    int32_t* o_ids;
+    int32_t* o_ids;        // optional caller copies of the routing outputs
     float* o_w;
+};
+
+struct BucketParams {
+    int T, E, k, has_shared;
+    int tiles_gu_r, tiles_gu_s, tiles_dn;   // row tiles per item list
+    int pieces_dn_r, pieces_dn_s;           // K-pieces of a routed / the shared down item
+    Workspace ws;
     int32_t* o_counts;
     int32_t* o_offsets;
     int32_t* o_sorted;
 };
 
-// Dequantising GEMM over (expert, row tile, token group) work items.
-// gate_up: set 0 = gate rows [f0, f0+32), set 1 = up rows [f0, f0+32), K = d,
-//          B = xperm rows (tokens), epilogue SwiGLU -> act.
-// down:    set 0 = down rows [r0, r0+32), set 1 = rows [r0+32, r0+64), K = F,
-//          B = act rows (slots), epilogue w * o atomically added to y.
+// Dequantising GEMM over (expert, row tile, token group) items of one list.
+// An item covers 64 rows of each of two row-sets; wave w of the work-group
+// owns row block (w >> 1) (32 rows) and K-half (w & 1).
+// gate_up: set 0 = gate rows [f0, f0+64), set 1 = up rows [f0, f0+64), K = d,
+//          B = xperm rows (tokens), epilogue SwiGLU -> act (fp16).
+// down:    set 0 = rows [r0, r0+64), set 1 = rows [r0+64, r0+128), K = F,
+//          B = act rows (slots), epilogue w * o atomically added to y (fp32).
 struct GemmParams {
     const DevBlock* blocks;   // [n_total*3]
     int E, k, T, d;
     int F, Fs;                // routed / shared ffn (Fs = 0: none)
+    int has_shared;
     int tiles_r, tiles_s;     // row tiles per routed expert / for the shared expert
-    int n_work;               // E*tiles_r + tiles_s (grid.x may be padded above it)
+    int pieces_r, pieces_s;   // K-pieces per row tile (down only; gate_up: 1)
+    int list;                 // LIST_*
     Workspace ws;
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
     int lds_stripe;           // LDS bytes reserved for the LUT stripe / reduction
-    int min_count;            // work items with fewer tokens than this exit
-    int max_count;            // work items with more tokens than this exit
+    uint32_t b_bytes;         // size of the B-operand buffer (xperm or act)
     float* y;
 };
 
-hipError_t launch_init_ws(const Workspace& ws, int max_T, hipStream_t s);
+hipError_t launch_init_ws(const Workspace& ws, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
-// tile_tokens: 32 (one MFMA token tile per work item) or 128 (four tiles).
-hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes,
-                       int n_zgroups, hipStream_t s);
+hipError_t launch_bucket(const BucketParams& p, hipStream_t s);
+// tile_tokens: 32 (one MFMA token tile per item) or 128 (four tiles).
+hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
+                       hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
                            hipStream_t s);
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
@@ -82,6 +95,10 @@ hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int
 // LDS bytes of the gemm kernels for a largest bitwidth bmax.
 int gemm_lds_bytes(int bmax);
 
-constexpr int kTokInfoBytes = 128 * 12;   // per-work-item token rows / outputs / weights
+constexpr int kTokInfoBytes = 128 * 12;   // per-item token rows / outputs / weights
+constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
+constexpr int kRouteThreads = 512;
+constexpr int kBucketThreads = 1024;
+constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)
 
 }  // namespace pw

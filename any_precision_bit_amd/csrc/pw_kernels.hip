@@ -29,6 +29,8 @@
 // the same in-group column permutation, so the contraction is unchanged.
 #include <hip/hip_runtime.h>
 
+#include <climits>
+
 #include "pw.h"
 #include "pw_internal.h"
 
@@ -51,6 +53,24 @@ __device__ __forceinline__ float h2f(uint16_t u) {
 }
 __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);   // round to nearest even
+}
+
+// Raw buffer loads: an offset at or past num_records reads 0 without touching
+// memory. Every plane / activation load of the hot loop is issued
+// unconditionally this way (absent planes get num_records 0, lanes past K an
+// out-of-range offset), so the compiler can count outstanding loads exactly and
+// wait only for the chunk it is about to use.
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    // base and size are wave-uniform: keep the descriptor in scalar registers
+    const uint64_t b = (uint64_t)(size_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)nbytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(size_t)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
 // Position of column c (0..31) of a 32-column group in the permuted activation
@@ -78,31 +98,174 @@ __device__ __forceinline__ void add_pair(uint32_t xw, uint32_t ww, long long& ac
     }
 }
 
-template <typename Tv>
-__device__ __forceinline__ Tv load_relaxed(const Tv* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void fma_pair(uint32_t xw, uint32_t ww, float& acc, float& sab) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float xf = h2f((uint16_t)(xw >> (16 * h)));
+        const float wf = h2f((uint16_t)(ww >> (16 * h)));
+        acc = fmaf(xf, wf, acc);                 // the product of two fp16 values is exact in fp32
+        sab = fmaf(fabsf(xf), fabsf(wf), sab);
+    }
 }
 
-__global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
-    const int eg = blockIdx.x, t = blockIdx.y;
+// Key order of the top-k: larger value first, ties to the lower expert index.
+template <typename V>
+__device__ __forceinline__ bool key_gt(V va, int ea, V vb, int eb) {
+    return va > vb || (va == vb && ea < eb);
+}
+
+// fp32 logit and bound of every expert e = wave + NW*i of one token. A row is NB
+// blocks of 512 columns (8 per lane); 32/NB rows are in flight per wave.
+template <int NB>
+__device__ __forceinline__ void approx_logits(const RouteParams& p, const uint16_t* s_x, float* s_apx,
+                                              float* s_bnd, int wave, int lane) {
+    constexpr int NW = kRouteThreads / 64;
+    constexpr int BATCH = NB >= 32 ? 1 : 32 / NB;
+    const int d = p.d, E = p.E;
+    for (int e0 = wave; e0 < E; e0 += NW * BATCH) {
+        uint4 w[BATCH][NB];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int e = e0 + NW * j;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int c = lane * 8 + 512 * i;
+                w[j][i] = (e < E && c < d) ? *(const uint4*)(p.wr + (size_t)e * d + c) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int e = e0 + NW * j;
+            if (e >= E) break;
+            float acc = 0.0f, sab = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int c = lane * 8 + 512 * i;
+                if (c < d) {
+                    const uint4 xv = *(const uint4*)(s_x + c);
+                    fma_pair(xv.x, w[j][i].x, acc, sab);
+                    fma_pair(xv.y, w[j][i].y, acc, sab);
+                    fma_pair(xv.z, w[j][i].z, acc, sab);
+                    fma_pair(xv.w, w[j][i].w, acc, sab);
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                acc += __shfl_xor(acc, off);
+                sab += __shfl_xor(sab, off);
+            }
+            if (lane == 0) {
+                const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
+                s_apx[e] = acc + bf;
+                s_bnd[e] = sab + fabsf(bf);
+            }
+        }
+    }
+}
+
+// One work-group per token. Selection is exact although the bulk of the logits
+// is computed in fp32: every fp32 logit A_e is within delta of the exact value
+// L_e, so any expert of the exact top-k has A_e >= a_k - 2*delta, a_k being the
+// k-th largest A. Only those candidates are recomputed exactly (int64 in units
+// of 2^-48) and the top-k is taken over their exact values.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
+    constexpr int NW = kRouteThreads / 64;
+    const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
-    const uint16_t* xr = p.x + (size_t)t * d;
-    __shared__ int s_flag;
-    __shared__ int s_cnt[PW_MAX_EXPERTS];
-    __shared__ int s_off[PW_MAX_EXPERTS + 1];
+    __shared__ __align__(16) uint16_t s_x[kMaxModel];
+    __shared__ float s_apx[PW_MAX_EXPERTS];
+    __shared__ float s_bnd[PW_MAX_EXPERTS];
+    __shared__ int s_cand[PW_MAX_EXPERTS];
+    __shared__ long long s_ex[PW_MAX_EXPERTS];
+    __shared__ int s_ncand;
 
-    // ---- exact logits of this group's experts: one wave per expert
-    const int e_begin = eg * p.epb;
-    const int e_end = min(E, e_begin + p.epb);
-    for (int e = e_begin + wave; e < e_end; e += 4) {
+    const uint16_t* xr = p.x + (size_t)t * d;
+    for (int c = tid * 8; c < d; c += kRouteThreads * 8) *(uint4*)(s_x + c) = *(const uint4*)(xr + c);
+    for (int c = tid; c < d; c += kRouteThreads) {
+        p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
+        p.y[(size_t)t * d + c] = 0.0f;
+    }
+    __syncthreads();
+
+    // ---- fp32 logits and their error bound, one wave per expert; a wave issues
+    // the weight rows of a batch of its experts before reducing any of them
+    switch ((d + 511) >> 9) {
+        case 1: approx_logits<1>(p, s_x, s_apx, s_bnd, wave, lane); break;
+        case 2: approx_logits<2>(p, s_x, s_apx, s_bnd, wave, lane); break;
+        case 3: case 4: approx_logits<4>(p, s_x, s_apx, s_bnd, wave, lane); break;
+        case 5: case 6: case 7: case 8: approx_logits<8>(p, s_x, s_apx, s_bnd, wave, lane); break;
+        default: approx_logits<16>(p, s_x, s_apx, s_bnd, wave, lane); break;
+    }
+    __syncthreads();
+
+    // ---- candidates: A_e >= a_k - 2*delta
+    if (wave == 0) {
+        float v[PW_MAX_EXPERTS / 64];
+        bool taken[PW_MAX_EXPERTS / 64];
+        float bm = 0.0f;
+#pragma unroll
+        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
+            const int e = lane + 64 * q;
+            v[q] = e < E ? s_apx[e] : -INFINITY;
+            taken[q] = e >= E;
+            if (e < E) bm = fmaxf(bm, s_bnd[e]);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+        float ak = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
+                const int e = lane + 64 * q;
+                if (!taken[q] && key_gt(v[q], e, bv, be)) {
+                    bv = v[q];
+                    be = e;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oe = __shfl_xor(be, off);
+                if (key_gt(ov, oe, bv, be)) {
+                    bv = ov;
+                    be = oe;
+                }
+            }
+            ak = bv;
+#pragma unroll
+            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q)
+                if (be == lane + 64 * q) taken[q] = true;
+        }
+        // |A_e - L_e| <= gamma_(d+1) * sum|x w| + |bias|-rounding: (d+2) * 2^-24 covers both
+        const float delta = bm * (float)(d + 2) * 5.9604645e-8f * 1.001f + 1e-30f;
+        const float tau = ak - 2.0f * delta - fabsf(ak) * 2.4e-7f - 2.0f * delta * 2.4e-7f;
+        int base = 0;
+#pragma unroll
+        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
+            const int e = lane + 64 * q;
+            const bool c = e < E && v[q] >= tau;
+            const unsigned long long m = __ballot(c);
+            if (c) s_cand[base + __popcll(m & __lanemask_lt())] = e;
+            base += __popcll(m);
+        }
+        if (lane == 0) s_ncand = base;
+    }
+    __syncthreads();
+
+    // ---- exact logits of the candidates, one wave per candidate
+    const int nc = s_ncand;
+    for (int ci = wave; ci < nc; ci += NW) {
+        const int e = s_cand[ci];
         const uint16_t* wrow = p.wr + (size_t)e * d;
         long long acc = 0;
         float sab = 0.0f;
         int bad = 0;
         for (int c = lane * 8; c < d; c += 512) {
-            const uint4 xv = *(const uint4*)(xr + c);
             const uint4 wv = *(const uint4*)(wrow + c);
+            const uint4 xv = *(const uint4*)(s_x + c);
             add_pair(xv.x, wv.x, acc, sab, bad);
             add_pair(xv.y, wv.y, acc, sab, bad);
             add_pair(xv.z, wv.z, acc, sab, bad);
@@ -121,58 +284,36 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
                 if (!bad) acc += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
                 sab += fabsf(bf);
             }
-            // the fp32 bound has relative error below d*2^-24, far inside the margin
+            // sum |x w| < 2^15 keeps every partial sum inside int64 (fp32 bound, wide margin)
             if (bad || !(sab < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
-            p.ws.logits[(size_t)t * E + e] = acc;
+            s_ex[ci] = acc;
         }
     }
-
-    // ---- permuted copy of x (MFMA B-operand layout) and zeroed y, once per token
-    if (eg == 0) {
-        for (int c = tid; c < d; c += 256) {
-            p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
-            p.y[(size_t)t * d + c] = 0.0f;
-        }
-    }
-
-    // ---- last workgroup of this token selects its experts
-    __threadfence();
     __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(&p.ws.tok_cnt[t], 1u);
-        s_flag = (prev == (unsigned)(p.n_eg - 1));
-    }
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
 
+    // ---- exact top-k over the candidates, softmax over the selected logits
     if (wave == 0) {
-        long long v[PW_MAX_EXPERTS / 64];
-        bool taken[PW_MAX_EXPERTS / 64];
-#pragma unroll
-        for (int j = 0; j < PW_MAX_EXPERTS / 64; ++j) {
-            const int e = lane + 64 * j;
-            v[j] = (e < E) ? load_relaxed(&p.ws.logits[(size_t)t * E + e]) : 0;
-            taken[j] = (e >= E);
-        }
         long long selv[PW_MAX_TOP_K];
         int sele[PW_MAX_TOP_K];
+        bool taken[PW_MAX_EXPERTS / 64];
+#pragma unroll
+        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) taken[q] = (lane + 64 * q) >= nc;
         for (int j = 0; j < k; ++j) {
             long long bv = LLONG_MIN;
             int be = 0x7fffffff;
 #pragma unroll
             for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-                const int e = lane + 64 * q;
-                if (!taken[q] && (v[q] > bv || (v[q] == bv && e < be))) {
-                    bv = v[q];
-                    be = e;
+                const int ci = lane + 64 * q;
+                if (!taken[q] && key_gt(s_ex[ci], s_cand[ci], bv, be)) {
+                    bv = s_ex[ci];
+                    be = s_cand[ci];
                 }
             }
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) {
                 const long long ov = __shfl_xor(bv, off);
                 const int oe = __shfl_xor(be, off);
-                if (ov > bv || (ov == bv && oe < be)) {
+                if (key_gt(ov, oe, bv, be)) {
                     bv = ov;
                     be = oe;
                 }
@@ -180,8 +321,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
             selv[j] = bv;
             sele[j] = be;
 #pragma unroll
-            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q)
-                if (be == lane + 64 * q) taken[q] = true;
+            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
+                const int ci = lane + 64 * q;
+                if (ci < nc && s_cand[ci] == be) taken[q] = true;
+            }
         }
         if (lane == 0) {
             float l[PW_MAX_TOP_K], ex[PW_MAX_TOP_K];
@@ -198,100 +341,147 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
                 if (p.o_ids) p.o_ids[(size_t)t * k + j] = sele[j];
                 if (p.o_w) p.o_w[(size_t)t * k + j] = wj;
             }
-            p.ws.tok_cnt[t] = 0u;   // ready for the next call
         }
     }
+}
 
-    // ---- last workgroup of the call: stable bucket sort of the T*k assignments
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(p.ws.glob_cnt, 1u);
-        s_flag = (prev == (unsigned)(p.T - 1));
+// ============================================================================ bucket sort + work lists
+
+// Exclusive scan over the 1024 threads of the bucket kernel; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
     }
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-
-    const int n = p.T * k;
-    for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) atomicAdd(&s_cnt[load_relaxed(&p.ws.ids[i])], 1);
+    if (lane == 63) s_tmp[wave] = inc;
     __syncthreads();
     if (wave == 0) {
-        // exclusive scan over E <= 256 counts: 4 consecutive experts per lane
-        int c4[4], loc = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane * 4 + j;
-            c4[j] = (e < E) ? s_cnt[e] : 0;
-            loc += c4[j];
-        }
-        int inc = loc;
+        const int tv = lane < kBucketThreads / 64 ? s_tmp[lane] : 0;
+        int ti = tv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(inc, off);
-            if (lane >= off) inc += o;
+            const int o = __shfl_up(ti, off);
+            if (lane >= off) ti += o;
         }
-        int run = inc - loc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane * 4 + j;
-            if (e < E) s_off[e] = run;
-            run += c4[j];
-        }
-        if (lane == 63) s_off[E] = inc;
+        if (lane < kBucketThreads / 64) s_tmp[32 + lane] = ti - tv;
+        if (lane == kBucketThreads / 64 - 1) s_tmp[64] = ti;
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += 256) {
+    const int res = inc - v + s_tmp[32 + wave];
+    *total = s_tmp[64];
+    __syncthreads();
+    return res;
+}
+
+// One work-group: a stable counting sort of the T*k assignments by expert
+// (counts, exclusive offsets, assignments in ascending (t, j) per expert), and
+// the per-expert item prefix of each gemm work list.
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketParams p) {
+    constexpr int NW = kBucketThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = p.E, n = p.T * p.k;
+    __shared__ int s_cnt[PW_MAX_EXPERTS];
+    __shared__ int s_off[PW_MAX_EXPERTS + 1];
+    __shared__ int s_run[PW_MAX_EXPERTS];
+    __shared__ int s_wc[NW * PW_MAX_EXPERTS];
+    __shared__ int s_tmp[80];
+
+    const bool one_chunk = n <= kBucketThreads;
+    const int my_e = (one_chunk && tid < n) ? p.ws.ids[tid] : 0;
+    for (int e = tid; e < E; e += kBucketThreads) s_cnt[e] = 0;
+    __syncthreads();
+    if (one_chunk) {
+        if (tid < n) atomicAdd(&s_cnt[my_e], 1);
+    } else {
+        for (int i = tid; i < n; i += kBucketThreads) atomicAdd(&s_cnt[p.ws.ids[i]], 1);
+    }
+    __syncthreads();
+    {
+        int tot;
+        const int v = tid < E ? s_cnt[tid] : 0;
+        const int ex = block_excl_scan(v, s_tmp, &tot);
+        if (tid < E) s_off[tid] = ex;
+        if (tid == 0) s_off[E] = tot;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kBucketThreads) {
         p.ws.offsets[e] = s_off[e];
         if (p.o_offsets) p.o_offsets[e] = s_off[e];
         if (e < E) {
             p.ws.counts[e] = s_cnt[e];
             if (p.o_counts) p.o_counts[e] = s_cnt[e];
+            s_run[e] = s_off[e];
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        // s_cnt becomes the running insert position of each expert
-        for (int e = lane; e < E; e += 64) s_cnt[e] = s_off[e];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        for (int base = 0; base < n; base += 64) {
-            const int i = base + lane;
-            const bool valid = i < n;
-            const int e = valid ? load_relaxed(&p.ws.ids[i]) : 0;
-            unsigned long long same = __ballot(valid);
+    for (int base = 0; base < n; base += kBucketThreads) {
+        for (int j = tid; j < NW * E; j += kBucketThreads) s_wc[j] = 0;
+        __syncthreads();
+        const int i = base + tid;
+        const bool valid = i < n;
+        const int e = valid ? (one_chunk ? my_e : p.ws.ids[i]) : 0;
+        unsigned long long same = __ballot(valid);
 #pragma unroll
-            for (int bit = 0; bit < 8; ++bit) {
-                const unsigned long long bb = __ballot(valid && ((e >> bit) & 1));
-                same &= ((e >> bit) & 1) ? bb : ~bb;
-            }
-            const int rank = __popcll(same & __lanemask_lt());
-            const int pos = s_cnt[e] + rank;
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            if (valid) {
-                p.ws.sorted[pos] = i;
-                if (p.o_sorted) p.o_sorted[pos] = i;
-                if ((same >> lane) == 1ull) s_cnt[e] += __popcll(same);   // highest lane of its group
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-            __builtin_amdgcn_wave_barrier();
+        for (int bit = 0; bit < 8; ++bit) {
+            const unsigned long long bb = __ballot(valid && ((e >> bit) & 1));
+            same &= ((e >> bit) & 1) ? bb : ~bb;
         }
-        if (lane == 0) *p.ws.glob_cnt = 0u;
+        const int rank = __popcll(same & __lanemask_lt());
+        if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kBucketThreads) {
+            int run = s_run[ee];
+            for (int w = 0; w < NW; ++w) {
+                const int c = s_wc[w * E + ee];
+                s_wc[w * E + ee] = run;
+                run += c;
+            }
+            s_run[ee] = run;
+        }
+        __syncthreads();
+        if (valid) {
+            const int pos = s_wc[wave * E + e] + rank;
+            p.ws.sorted[pos] = i;
+            if (p.o_sorted) p.o_sorted[pos] = i;
+        }
+        __syncthreads();
+    }
+
+    // ---- work lists: list position 0 is the shared expert (long items first)
+    const int npos = E + p.has_shared;
+    int cnt = 0, tgu = 0, pdn = 1;
+    if (tid < npos) {
+        const bool sh = p.has_shared && tid == 0;
+        const int ex = sh ? E : tid - p.has_shared;
+        cnt = sh ? p.T : s_cnt[ex];
+        tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
+        pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
+    }
+    const int small = (cnt >= 1 && cnt <= 32) ? 1 : 0;
+    const int groups = cnt > 32 ? (cnt + 127) / 128 : 0;
+    const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn, groups * p.tiles_dn * pdn};
+    const int stride = E + 2;
+    for (int l = 0; l < N_LISTS; ++l) {
+        int tot;
+        const int ex = block_excl_scan(tid < npos ? nitems[l] : 0, s_tmp, &tot);
+        if (tid < npos) p.ws.prefix[l * stride + tid] = ex;
+        if (tid == 0) p.ws.prefix[l * stride + npos] = tot;
     }
 }
 
 // ============================================================================ dequant core
 
-// Transposes the b plane words of one 32-column group into index words:
-// out[i] byte k = index of column 8k+i (plane p is bit b-1-p of the index).
-template <int B>
-__device__ __forceinline__ void planes_to_indices(const uint32_t (&pl)[8], uint32_t (&rw)[8]) {
+// Transposes the plane words of one 32-column group into index words.
+// Slot s of `sl` holds plane s - (8 - b) (slots below 8 - b are zero), so slot
+// s carries bit 7 - s of the b-bit index for every b: out[i] byte k = index of
+// column 8k + i. An 8x8 bit transpose inside every byte: swap the
+// off-diagonal 4x4, 2x2 and 1x1 blocks.
+__device__ __forceinline__ void slots_to_indices(const uint32_t (&sl)[8], uint32_t (&rw)[8]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) rw[q] = (q < B) ? pl[B - 1 - q] : 0u;
-    // 8x8 bit transpose inside every byte: swap the off-diagonal 4x4, 2x2, 1x1 blocks
+    for (int q = 0; q < 8; ++q) rw[q] = sl[7 - q];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t a = rw[q], b = rw[q + 4];
@@ -315,78 +505,82 @@ __device__ __forceinline__ void planes_to_indices(const uint32_t (&pl)[8], uint3
     }
 }
 
-// A fragments of four MFMA steps from one 32-column dword per plane:
-// a[m] half 2k+e = LUT[index of column 8k + 2m + e]. `slot` is the lane's LDS
-// address of stripe entry 0 (segment base + (g*32 + r)*4); byte 1 of it is
-// replaced by the index, i.e. entry idx sits idx*256 bytes further.
-template <int B>
-__device__ __forceinline__ void dq_dword(const uint32_t (&pl)[8], uint32_t slot, int hoff,
-                                         half8 (&a)[4]) {
-    uint32_t rw[8];
-    planes_to_indices<B>(pl, rw);
+// A fragment of MFMA step m from the index words of one 32-column group:
+// half 2k+e = LUT[index of column 8k + 2m + e]. `slot` is the lane's LDS address
+// of stripe entry 0 (segment base + row slot * 4); byte 1 of it is replaced by
+// the index, i.e. entry idx sits idx*256 bytes further. hoff selects the row-set
+// (0: low half, 2: high half of the stripe dword).
+__device__ __forceinline__ half8 lut_fragment(const uint32_t (&rw)[8], int m, uint32_t slot, int hoff) {
+    half8 a;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t addr =
-                    __builtin_amdgcn_perm(rw[2 * m + e], slot, 0x03020400u | (uint32_t)(kk << 8));
-                a[m][2 * kk + e] = *(lds_half*)(size_t)(addr + hoff);
-            }
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t addr =
+                __builtin_amdgcn_perm(rw[2 * m + e], slot, 0x03020400u | (uint32_t)(kk << 8));
+            a[2 * kk + e] = *(lds_half*)(size_t)(addr + hoff);
         }
     }
+    return a;
 }
 
-__device__ __forceinline__ void dq_dword_rt(int b, const uint32_t (&pl)[8], uint32_t slot, int hoff,
-                                            half8 (&a)[4]) {
-    switch (b) {
-        case 1: dq_dword<1>(pl, slot, hoff, a); break;
-        case 2: dq_dword<2>(pl, slot, hoff, a); break;
-        case 3: dq_dword<3>(pl, slot, hoff, a); break;
-        case 4: dq_dword<4>(pl, slot, hoff, a); break;
-        case 5: dq_dword<5>(pl, slot, hoff, a); break;
-        case 6: dq_dword<6>(pl, slot, hoff, a); break;
-        case 7: dq_dword<7>(pl, slot, hoff, a); break;
-        default: dq_dword<8>(pl, slot, hoff, a); break;
-    }
-}
-
-// 8 LUT entries [c8, c8+8) of one row (zeros past 2^b).
-__device__ __forceinline__ void load_lut8(const uint16_t* row, int b, int c8, uint32_t (&v)[8]) {
+// 8 LUT entries [c8, c8+8) of one row as four packed fp16 pairs (zeros past 2^b).
+__device__ __forceinline__ uint4 load_lut8(const uint16_t* row, int b, int c8) {
     const int n = 1 << b;
-    if (b >= 3) {
-        uint4 q = make_uint4(0, 0, 0, 0);
-        if (c8 < n) q = *(const uint4*)(row + c8);
-        v[0] = q.x & 0xFFFF; v[1] = q.x >> 16; v[2] = q.y & 0xFFFF; v[3] = q.y >> 16;
-        v[4] = q.z & 0xFFFF; v[5] = q.z >> 16; v[6] = q.w & 0xFFFF; v[7] = q.w >> 16;
-    } else {
+    if (b >= 3) return c8 < n ? *(const uint4*)(row + c8) : make_uint4(0, 0, 0, 0);
+    uint32_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (c8 + i < n) ? row[c8 + i] : 0u;
+    for (int i = 0; i < 8; ++i) v[i] = (c8 + i < n) ? row[c8 + i] : 0u;
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+}
+
+// Writes 8 consecutive stripe entries (idx = c8..c8+7) of one row slot:
+// dword (idx*64 + row) = {set0 LUT[row][idx], set1 LUT[row][idx]}.
+__device__ __forceinline__ void write_stripe8(uint32_t* stripe, int c8, int row, int nidx, uint4 a, uint4 b) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = c8 + 2 * i;
+        if (idx < nidx) stripe[idx * 64 + row] = (av[i] & 0xFFFFu) | (bv[i] << 16);
+        if (idx + 1 < nidx) stripe[(idx + 1) * 64 + row] = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
     }
 }
 
-// Stages the LUT rows of both row-sets into the LDS stripe (two copies, one per
-// lane half g), cooperatively over nthreads threads.
-__device__ __forceinline__ void stage_luts(uint32_t* stripe, const uint16_t* lut0, int b0,
-                                           const uint16_t* lut1, int b1, int tid, int nthreads) {
+// Stages the LUTs of 64 rows of both row-sets into the LDS stripe. Loads are
+// issued in rounds of 4 per thread and set before their LDS writes: one memory
+// round trip for b <= 7, two for b = 8.
+__device__ __forceinline__ void stage_luts64(uint32_t* stripe, const uint16_t* lut0, int b0,
+                                             const uint16_t* lut1, int b1, int tid) {
+    constexpr int RIT = 4;
     const int bmax = b0 > b1 ? b0 : b1;
-    const int nc8 = (1 << bmax) >= 8 ? (1 << bmax) / 8 : 1;
-    for (int j = tid; j < nc8 * 32; j += nthreads) {
-        const int r = j & 31, c = j >> 5;
-        uint32_t v0[8], v1[8];
-        load_lut8(lut0 + ((size_t)r << b0), b0, c * 8, v0);
-        load_lut8(lut1 + ((size_t)r << b1), b1, c * 8, v1);
-        const int first = (j >> 5) & 1;   // alternate copies so a wave's halves hit different banks
+    const int nidx = 1 << bmax;
+    const int total = (nidx >= 8 ? nidx / 8 : 1) * 64;
+    for (int base = 0; base < total; base += RIT * 256) {
+        uint4 v0[RIT], v1[RIT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int idx = c * 8 + i;
-            if (idx < (1 << bmax)) {
-                const uint32_t dw = v0[i] | (v1[i] << 16);
-                stripe[idx * 64 + first * 32 + r] = dw;
-                stripe[idx * 64 + (1 - first) * 32 + r] = dw;
+        for (int it = 0; it < RIT; ++it) {
+            const int j = base + tid + it * 256;
+            if (j < total) {
+                const int r = j & 63, c8 = (j >> 6) * 8;
+                v0[it] = load_lut8(lut0 + ((size_t)r << b0), b0, c8);
+                v1[it] = load_lut8(lut1 + ((size_t)r << b1), b1, c8);
             }
         }
+#pragma unroll
+        for (int it = 0; it < RIT; ++it) {
+            const int j = base + tid + it * 256;
+            if (j < total) write_stripe8(stripe, (j >> 6) * 8, j & 63, nidx, v0[it], v1[it]);
+        }
+    }
+}
+
+// Same layout for 32 rows of one LUT (both halves), one wave, plain loop.
+__device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* lut, int b, int lane) {
+    const int nidx = 1 << b;
+    const int total = (nidx >= 8 ? nidx / 8 : 1) * 32;
+    for (int j = lane; j < total; j += 64) {
+        const uint4 v = load_lut8(lut + ((size_t)(j & 31) << b), b, (j >> 5) * 8);
+        write_stripe8(stripe, (j >> 5) * 8, j & 31, nidx, v, v);
     }
 }
 
@@ -396,197 +590,287 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int dw) {
 
 // ============================================================================ gemm
 
-// MODE 0: gate_up, MODE 1: down. NT: MFMA token tiles of 32 per work item.
+// One work item of a list, decoded from its index.
+struct Item {
+    int ex, tile, grp;        // expert (E = shared), row tile, token group
+    int n_tok, tbase, nl;     // tokens of the expert, first token of the group, tokens here
+    int K, R;                 // columns / rows of the block
+    int kbase, klen;          // K range of this item
+    int rows0, rows1;         // first row of set 0 / set 1
+    const DevBlock* blk0;
+    const DevBlock* blk1;
+};
+
+// Token rows of one item for thread tid (tid < nl): B row, output row, weight.
+struct TokInfo {
+    int brow, orow;
+    float w;
+};
+
+template <int MODE>
+__device__ __forceinline__ TokInfo fetch_tokinfo(const GemmParams& p, const Item& it, int tid) {
+    TokInfo tk{0, 0, 0.0f};
+    if (tid < it.nl) {
+        const bool sh = it.ex == p.E;
+        const int tkn = it.tbase + tid;
+        const int slot = sh ? (p.shared_base + tkn) : (p.ws.offsets[it.ex] + tkn);
+        if (MODE == 0) {
+            tk.brow = sh ? tkn : p.ws.sorted[slot] / p.k;   // token: xperm row
+            tk.orow = slot;                                 // act row
+        } else {
+            const int asg = sh ? 0 : p.ws.sorted[slot];
+            tk.brow = slot;                                 // act row
+            tk.orow = sh ? tkn : asg / p.k;                 // token: y row
+            tk.w = sh ? 1.0f : p.ws.w[asg];
+        }
+    }
+    return tk;
+}
+
+template <int MODE, int NT>
+__device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pre, int npos, int item) {
+    int lo = 0, hi = npos - 1;   // last position with s_pre[pos] <= item
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    lo = __builtin_amdgcn_readfirstlane(lo);   // uniform: keep the item in scalar registers
+    Item it;
+    const bool sh = p.has_shared && lo == 0;
+    it.ex = sh ? p.E : lo - p.has_shared;
+    const int tiles = sh ? p.tiles_s : p.tiles_r;
+    const int pieces = sh ? p.pieces_s : p.pieces_r;
+    const int local = __builtin_amdgcn_readfirstlane(item - s_pre[lo]);
+    it.tile = local % tiles;
+    const int piece = (local / tiles) % pieces;
+    it.grp = local / tiles / pieces;
+    it.n_tok = sh ? p.T : p.ws.counts[it.ex];
+    it.tbase = it.grp * 32 * NT;
+    it.nl = min(32 * NT, it.n_tok - it.tbase);
+    if (MODE == 0) {
+        it.K = p.d;
+        it.R = sh ? p.Fs : p.F;
+        it.rows0 = it.rows1 = it.tile * 64;
+        it.blk0 = &p.blocks[it.ex * 3 + 0];
+        it.blk1 = &p.blocks[it.ex * 3 + 1];
+    } else {
+        it.K = sh ? p.Fs : p.F;
+        it.R = p.d;
+        it.rows0 = it.tile * 128;
+        it.rows1 = it.tile * 128 + 64;
+        it.blk0 = it.blk1 = &p.blocks[it.ex * 3 + 2];
+    }
+    it.kbase = piece * kDownPiece;
+    it.klen = min(it.K - it.kbase, MODE == 0 ? it.K : kDownPiece);
+    return it;
+}
+
+// Persistent work-group of 4 waves over the items of one list. Wave w owns row
+// block rb = w >> 1 (32 rows of each set) and K-half kh = w & 1 (256-column
+// chunks kh, kh+2, ...). MODE 0: gate_up, MODE 1: down. NT: token tiles of 32.
 template <int MODE, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bid = blockIdx.x;
-    if (bid >= p.n_work) return;
-    int e, tile;
-    if (bid < p.E * p.tiles_r) {
-        e = bid / p.tiles_r;
-        tile = bid - e * p.tiles_r;
-    } else {
-        e = p.E;
-        tile = bid - p.E * p.tiles_r;
-    }
-    const bool shared = (e == p.E);
-    const int n_tok = shared ? p.T : p.ws.counts[e];
-    if (n_tok < p.min_count || n_tok > p.max_count) return;
-    const int tbase = blockIdx.y * (32 * NT);
-    if (tbase >= n_tok) return;
-    const int nl = min(32 * NT, n_tok - tbase);
-    const int ntl = (nl + 31) >> 5;
-
-    const DevBlock* blk0 = &p.blocks[e * 3 + (MODE == 0 ? 0 : 2)];
-    const DevBlock* blk1 = &p.blocks[e * 3 + (MODE == 0 ? 1 : 2)];
-    const int rb0 = MODE == 0 ? tile * 32 : tile * 64;
-    const int rb1 = MODE == 0 ? tile * 32 : tile * 64 + 32;
-    const int K = MODE == 0 ? p.d : (shared ? p.Fs : p.F);
-    const int b0 = blk0->bits, b1 = blk1->bits;
-    const int Kb = K >> 3;
-
-    // ---- token rows of this work item
+    const int r = lane & 31, g = lane >> 5, rb = wave >> 1, kh = wave & 1;
     int* s_brow = (int*)(smem + p.lds_stripe);
     int* s_orow = s_brow + 128;
     float* s_ow = (float*)(s_orow + 128);
-    for (int i = tid; i < nl; i += 256) {
-        const int slot = shared ? (p.shared_base + tbase + i) : (p.ws.offsets[e] + tbase + i);
-        if (MODE == 0) {
-            s_brow[i] = shared ? (tbase + i) : p.ws.sorted[slot] / p.k;   // token (xperm row)
-            s_orow[i] = slot;                                              // act row
-        } else {
-            const int asg = shared ? 0 : p.ws.sorted[slot];
-            s_brow[i] = slot;                                              // act row
-            s_orow[i] = shared ? (tbase + i) : asg / p.k;                  // token (y row)
-            s_ow[i] = shared ? 1.0f : p.ws.w[asg];
-        }
-    }
-
-    // ---- plane bases are uniform (SGPRs); each lane adds one 32-bit offset per set
-    const int r = lane & 31, g = lane >> 5;
-    const uint32_t slot = lds_addr(smem) + (uint32_t)((g * 32 + r) * 4);
-    const int nch = (K + 255) >> 8;
-    const uint8_t* base0[8];
-    const uint8_t* base1[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        base0[q] = (const uint8_t*)blk0->planes[q];
-        base1[q] = (const uint8_t*)blk1->planes[q];
-    }
-    const uint32_t off0 = (uint32_t)((rb0 + r) * Kb + g * 16);
-    const uint32_t off1 = (uint32_t)((rb1 + r) * Kb + g * 16);
-    auto load_chunk = [&](int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
-        const bool vg = (ch * 256 + g * 128) < K;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (q < b0 && vg) c0[q] = *(const uint4*)(base0[q] + (off0 + (uint32_t)ch * 32u));
-            if (q < b1 && vg) c1[q] = *(const uint4*)(base1[q] + (off1 + (uint32_t)ch * 32u));
+    int* s_pre = (int*)(smem + p.lds_stripe + kTokInfoBytes);
+    int* s_item = s_pre + PW_MAX_EXPERTS + 2;   // [0] first item, [1] reserved next item
+    const int npos = p.E + p.has_shared;
+    // Items are handed out by an atomic counter; each work-group holds one item in
+    // reserve so that its first chunk can be prefetched. The last work-group to
+    // leave resets the counters for the next launch.
+    uint32_t* cnt = p.ws.sched + 2 * p.list;
+    auto leave = [&]() {
+        if (tid == 0 && atomicAdd(cnt + 1, 1u) == gridDim.x - 1) {
+            atomicExch(cnt, 0u);
+            atomicExch(cnt + 1, 0u);
         }
     };
-    // ping-pong plane buffers: chunk ch in A while chunk ch+4 loads into B
-    uint4 pa0[8], pa1[8], pb0[8], pb1[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        pa0[q] = pa1[q] = pb0[q] = pb1[q] = make_uint4(0, 0, 0, 0);
-    }
-    if (wave < nch) load_chunk(wave, pa0, pa1);
-
-    stage_luts((uint32_t*)smem, (const uint16_t*)blk0->lut + ((size_t)rb0 << b0), b0,
-               (const uint16_t*)blk1->lut + ((size_t)rb1 << b1), b1, tid, 256);
+    for (int i = tid; i <= npos; i += 256) s_pre[i] = p.ws.prefix[p.list * (p.E + 2) + i];
+    if (tid == 0) s_item[0] = (int)atomicAdd(cnt, 1u);
     __syncthreads();
+    const int n_items = __builtin_amdgcn_readfirstlane(s_pre[npos]);
+    int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n_items) {
+        leave();
+        return;
+    }
 
+    const uint32_t slot = lds_addr(smem) + (uint32_t)((rb * 32 + r) * 4);
     const uint16_t* Bbase = MODE == 0 ? p.ws.xperm : p.ws.act;
     const int ldb = MODE == 0 ? p.d : p.ld_act;
-    uint32_t boff[NT];
-    bool bok[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int i = nt * 32 + r;
-        bok[nt] = i < nl;
-        boff[nt] = bok[nt] ? (uint32_t)(s_brow[i] * ldb + g * 128) : 0u;
-    }
+    const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(Bbase, p.b_bytes);
 
-    floatx16 acc0[NT], acc1[NT];
+    uint4 pa0[8], pa1[8], pb0[8], pb1[8];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        acc0[nt] = (floatx16)0.0f;
-        acc1[nt] = (floatx16)0.0f;
-    }
-    auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
-        const bool vg = (ch * 256 + g * 128) < K;
+    for (int q = 0; q < 8; ++q) pa0[q] = pa1[q] = pb0[q] = pb1[q] = make_uint4(0, 0, 0, 0);
+
+    // plane loads of chunk ch of an item into (c0, c1); lanes past K load nothing
+    // plane loads of chunk ch of an item into (c0, c1): slot q holds plane
+    // q - (8 - b); slots below 8 - b and lanes past K read zeros
+    auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
+        const int Kb = it.K >> 3;
+        const bool vg = (ch * 256 + g * 128) < it.klen;
+        const uint32_t nrec = (uint32_t)(it.R * Kb);
+        const int cb = (it.kbase >> 3) + g * 16 + ch * 32;
+        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + rb * 32 + r) * Kb + cb) : kOOB;
+        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + rb * 32 + r) * Kb + cb) : kOOB;
+        const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-            half8 bf[NT][4];
+        for (int q = 0; q < 8; ++q) {
+            c0[q] = buf_load16(make_rsrc((const void*)it.blk0->planes[q], q >= s0 ? nrec : 0u), off0);
+            c1[q] = buf_load16(make_rsrc((const void*)it.blk1->planes[q], q >= s1 ? nrec : 0u), off1);
+        }
+    };
+
+    Item it = decode_item<MODE, NT>(p, s_pre, npos, item);
+    if (kh < ((it.klen + 255) >> 8)) load_chunk(it, kh, pa0, pa1);
+    TokInfo tk = fetch_tokinfo<MODE>(p, it, tid);
+
+    while (true) {
+        const int nch = (it.klen + 255) >> 8;
+        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
+        const bool sh = it.ex == p.E;
+        const int ntl = (it.nl + 31) >> 5;
+        __syncthreads();   // the previous item's epilogue is done with LDS
+        int grab = 0;   // next item, reserved during this wave's last chunk
+        if (tid < it.nl) {
+            s_brow[tid] = tk.brow;
+            s_orow[tid] = tk.orow;
+            s_ow[tid] = tk.w;
+        }
+        stage_luts64((uint32_t*)smem, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
+                     (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
+        __syncthreads();
+
+        uint32_t boff[NT];
+        bool bok[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int i = nt * 32 + r;
+            bok[nt] = i < it.nl;
+            boff[nt] = bok[nt] ? (uint32_t)(s_brow[i] * ldb + g * 128) : 0u;
+        }
+        floatx16 acc0[NT], acc1[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc0[nt] = (floatx16)0.0f;
+            acc1[nt] = (floatx16)0.0f;
+        }
+
+        auto load_b = [&](int ch, int dw, half8 (&bf)[NT][4], bool vg) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
+                const uint32_t off = (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 256 + 32 * dw)) * 2u : kOOB;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) bf[nt][m] = (half8)(_Float16)0.0f;
-                if (nt < ntl && bok[nt] && vg) {
-                    const half8* src = (const half8*)(Bbase + (boff[nt] + (uint32_t)(ch * 256 + 32 * dw)));
+                for (int m = 0; m < 4; ++m) bf[nt][m] = __builtin_bit_cast(half8, buf_load16(brsrc, off + 16u * m));
+            }
+        };
+
+        // One 256-column chunk: for each of the four 32-column dwords, transpose the
+        // plane words of both sets, look the weights up and feed the MFMAs. The B
+        // fragments of dword dw+1 load while dword dw computes (two named buffers,
+        // the dword loop is unrolled). Lanes past K hold zero B fragments, so their
+        // A fragments need no masking.
+        auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
+            const bool vg = (ch * 256 + g * 128) < it.klen;
+            half8 bfr[2][NT][4];
+            load_b(ch, 0, bfr[0], vg);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) bf[nt][m] = src[m];
+            for (int dw = 0; dw < 4; ++dw) {
+                if (dw < 3) load_b(ch, dw + 1, bfr[(dw + 1) & 1], vg);
+                uint32_t w0[8], w1[8], rw0[8], rw1[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    w0[q] = word_of(c0[q], dw);
+                    w1[q] = word_of(c1[q], dw);
                 }
-            }
-            uint32_t w0[8], w1[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                w0[q] = word_of(c0[q], dw);
-                w1[q] = word_of(c1[q], dw);
-            }
-            half8 a0[4], a1[4];
-            dq_dword_rt(b0, w0, slot, 0, a0);
-            dq_dword_rt(b1, w1, slot, 2, a1);
-            if (!vg) {
+                slots_to_indices(w0, rw0);
+                slots_to_indices(w1, rw1);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    a0[m] = (half8)(_Float16)0.0f;
-                    a1[m] = (half8)(_Float16)0.0f;
-                }
-            }
+                    const half8 a0 = lut_fragment(rw0, m, slot, 0);
+                    const half8 a1 = lut_fragment(rw1, m, slot, 2);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    if (nt < ntl) {
-                        acc0[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[m], bf[nt][m], acc0[nt], 0, 0, 0);
-                        acc1[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[m], bf[nt][m], acc1[nt], 0, 0, 0);
+                    for (int nt = 0; nt < NT; ++nt) {
+                        if (nt < ntl) {
+                            acc0[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bfr[dw & 1][nt][m], acc0[nt], 0, 0, 0);
+                            acc1[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bfr[dw & 1][nt][m], acc1[nt], 0, 0, 0);
+                        }
                     }
                 }
             }
-        }
-    };
+        };
 
-    for (int ch = wave; ch < nch; ch += 8) {
-        if (ch + 4 < nch) load_chunk(ch + 4, pb0, pb1);
-        compute_chunk(ch, pa0, pa1);
-        if (ch + 4 >= nch) break;
-        if (ch + 8 < nch) load_chunk(ch + 8, pa0, pa1);
-        compute_chunk(ch + 4, pb0, pb1);
-    }
-
-    // ---- cross-wave K reduction through LDS, then the epilogue
-    float* red = (float*)smem;   // [4 waves][64 lanes][16]
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        if (nt >= ntl) break;
-        float s0[4], s1[4];
-#pragma unroll
-        for (int set = 0; set < 2; ++set) {
-            const floatx16& a = set == 0 ? acc0[nt] : acc1[nt];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) red[wave * 1024 + lane * 16 + v] = a[v];
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = tid + 256 * q;
-                const float sum = red[j] + red[1024 + j] + red[2048 + j] + red[3072 + j];
-                if (set == 0) s0[q] = sum; else s1[q] = sum;
-            }
-            __syncthreads();
+        // ping-pong over this wave's chunks kh, kh+2, ...: chunk in A while the next loads into B
+        if (kh >= nch && tid == 0) grab = (int)atomicAdd(cnt, 1u);
+        for (int ch = kh; ch < nch; ch += 4) {
+            if (ch + 2 < nch) load_chunk(it, ch + 2, pb0, pb1);
+            else if (tid == 0) grab = (int)atomicAdd(cnt, 1u);
+            compute_chunk(ch, pa0, pa1);
+            if (ch + 2 >= nch) break;
+            if (ch + 4 < nch) load_chunk(it, ch + 4, pa0, pa1);
+            else if (tid == 0) grab = (int)atomicAdd(cnt, 1u);
+            compute_chunk(ch + 2, pb0, pb1);
         }
+
+        // next item: decode and start its first chunk before this item's epilogue
+        if (tid == 0) s_item[1] = grab;
+        __syncthreads();             // s_item[1] is visible; every wave is done with the LUT stripe
+        const int next = __builtin_amdgcn_readfirstlane(s_item[1]);
+        Item nit = it;
+        TokInfo ntk = tk;
+        if (next < n_items) {
+            nit = decode_item<MODE, NT>(p, s_pre, npos, next);
+            if (kh < ((nit.klen + 255) >> 8)) load_chunk(nit, kh, pa0, pa1);
+            ntk = fetch_tokinfo<MODE>(p, nit, tid);
+        }
+
+        // ---- K-half reduction through LDS (odd waves hand over), epilogue on even waves
+        float* red = (float*)smem;   // [rb][set][16][64]
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = tid + 256 * q;
-            const int ln = j >> 4, reg = j & 15;
-            const int tok_i = nt * 32 + (ln & 31);
-            const int row = (reg >> 2) * 8 + (ln >> 5) * 4 + (reg & 3);
-            if (tok_i < nl) {
-                if (MODE == 0) {
-                    const float gv = s0[q], uv = s1[q];
-                    const float av = gv / (1.0f + expf(-gv)) * uv;
-                    p.ws.act[(size_t)s_orow[tok_i] * p.ld_act + rb0 + perm32(row)] = f2h(av);
-                } else {
-                    const float wv = s_ow[tok_i];
-                    float* yr = p.y + (size_t)s_orow[tok_i] * p.d;
-                    unsafeAtomicAdd(yr + rb0 + row, wv * s0[q]);
-                    unsafeAtomicAdd(yr + rb1 + row, wv * s1[q]);
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt >= ntl) break;
+            if (kh == 1) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    red[((rb * 2 + 0) * 16 + v) * 64 + lane] = acc0[nt][v];
+                    red[((rb * 2 + 1) * 16 + v) * 64 + lane] = acc1[nt][v];
                 }
             }
+            __syncthreads();
+            if (kh == 0) {
+                const int tok_i = nt * 32 + r;
+                if (tok_i < it.nl) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float s0 = acc0[nt][v] + red[((rb * 2 + 0) * 16 + v) * 64 + lane];
+                        const float s1 = acc1[nt][v] + red[((rb * 2 + 1) * 16 + v) * 64 + lane];
+                        const int row = rb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+                        if (MODE == 0) {
+                            const float av = s0 / (1.0f + expf(-s0)) * s1;
+                            const int f = it.rows0 + row;
+                            p.ws.act[(size_t)s_orow[tok_i] * p.ld_act + (f & ~31) + perm32(f & 31)] = f2h(av);
+                        } else {
+                            const float wv = s_ow[tok_i];
+                            float* yr = p.y + (size_t)s_orow[tok_i] * p.d;
+                            unsafeAtomicAdd(yr + it.rows0 + row, wv * s0);
+                            unsafeAtomicAdd(yr + it.rows1 + row, wv * s1);
+                        }
+                    }
+                }
+            }
+            if (nt + 1 < ntl) __syncthreads();
         }
+        if (next >= n_items) break;
+        item = next;
+        it = nit;
+        tk = ntk;
     }
+    leave();
 }
 
 // ============================================================================ residual / init / debug
@@ -597,13 +881,9 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
     if (i < n) out[i] = f2h(h2f(x[i]) + y[i]);
 }
 
-__global__ __launch_bounds__(256) void init_ws_kernel(Workspace ws, int max_T) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < max_T) ws.tok_cnt[i] = 0u;
-    if (i == 0) {
-        *ws.glob_cnt = 0u;
-        *ws.status = 0u;
-    }
+__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws) {
+    if (threadIdx.x == 0) *ws.status = 0u;
+    if (threadIdx.x < 2 * N_LISTS) ws.sched[threadIdx.x] = 0u;
 }
 
 struct DebugParams {
@@ -621,18 +901,20 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
     const int lane = threadIdx.x, r = lane & 31, g = lane >> 5;
     const int rb = blockIdx.x * 32;
     const int Kb = p.K >> 3;
-    const uint16_t* lut = p.lut + ((size_t)rb << p.b);
-    if (p.w_out) stage_luts((uint32_t*)smem, lut, p.b, lut, p.b, lane, 64);
+    if (p.w_out) {
+        const uint16_t* lut = p.lut + ((size_t)rb << p.b);
+        stage_lut32((uint32_t*)smem, lut, p.b, lane);
+    }
     __syncthreads();
-    const uint32_t slot = lds_addr(smem) + (uint32_t)((g * 32 + r) * 4);
+    const uint32_t slot = lds_addr(smem) + (uint32_t)(r * 4);
     for (int ch = 0; ch * 256 < p.K; ++ch) {
         const int c0 = ch * 256 + g * 128;
         if (c0 >= p.K) continue;
         uint4 q4[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 8; ++q) {   // slot q holds plane q - (8 - b)
             q4[q] = make_uint4(0, 0, 0, 0);
-            if (q < p.b) q4[q] = *(const uint4*)((const uint8_t*)p.planes[q] + (size_t)(rb + r) * Kb + ch * 32 + g * 16);
+            if (q >= 8 - p.b) q4[q] = *(const uint4*)((const uint8_t*)p.planes[q] + (size_t)(rb + r) * Kb + ch * 32 + g * 16);
         }
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
@@ -641,18 +923,9 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
             for (int q = 0; q < 8; ++q) w[q] = word_of(q4[q], dw);
             const int cg = c0 + 32 * dw;
             const size_t rowoff = (size_t)(rb + r) * p.K;
+            uint32_t rw[8];
+            slots_to_indices(w, rw);
             if (p.idx_out) {
-                uint32_t rw[8];
-                switch (p.b) {
-                    case 1: planes_to_indices<1>(w, rw); break;
-                    case 2: planes_to_indices<2>(w, rw); break;
-                    case 3: planes_to_indices<3>(w, rw); break;
-                    case 4: planes_to_indices<4>(w, rw); break;
-                    case 5: planes_to_indices<5>(w, rw); break;
-                    case 6: planes_to_indices<6>(w, rw); break;
-                    case 7: planes_to_indices<7>(w, rw); break;
-                    default: planes_to_indices<8>(w, rw); break;
-                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -660,16 +933,16 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
                         p.idx_out[rowoff + cg + 8 * kk + i] = (uint8_t)(rw[i] >> (8 * kk));
             }
             if (p.w_out) {
-                half8 a[4];
-                dq_dword_rt(p.b, w, slot, 0, a);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; ++m) {
+                    const half8 a = lut_fragment(rw, m, slot, 0);
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                         for (int e = 0; e < 2; ++e)
                             p.w_out[rowoff + cg + 8 * kk + 2 * m + e] =
-                                __builtin_bit_cast(uint16_t, (_Float16)a[m][2 * kk + e]);
+                                __builtin_bit_cast(uint16_t, (_Float16)a[2 * kk + e]);
+                }
             }
         }
     }
@@ -679,23 +952,27 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
 
 int gemm_lds_bytes(int bmax) {
     const int stripe = 256 << bmax;
-    const int red = 4 * 64 * 16 * 4;
-    return (stripe > red ? stripe : red) + kTokInfoBytes;
+    const int red = 2 * 2 * 16 * 64 * 4;
+    return (stripe > red ? stripe : red) + kTokInfoBytes + (PW_MAX_EXPERTS + 2) * 4 + 16;
 }
 
-hipError_t launch_init_ws(const Workspace& ws, int max_T, hipStream_t s) {
-    const int blocks = (max_T + 255) / 256 > 0 ? (max_T + 255) / 256 : 1;
-    hipLaunchKernelGGL(init_ws_kernel, dim3(blocks), dim3(256), 0, s, ws, max_T);
+hipError_t launch_init_ws(const Workspace& ws, hipStream_t s) {
+    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws);
     return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(route_kernel, dim3(p.n_eg, p.T), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(route_kernel, dim3(p.T), dim3(kRouteThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bucket(const BucketParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <int MODE, int NT>
-static hipError_t launch_gemm_t(const GemmParams& p, int lds_bytes, int nz, hipStream_t s) {
+static hipError_t launch_gemm_t(const GemmParams& p, int lds_bytes, int n_wg, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel<MODE, NT>,
@@ -703,19 +980,18 @@ static hipError_t launch_gemm_t(const GemmParams& p, int lds_bytes, int nz, hipS
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    const int gx = (p.n_work + 7) / 8 * 8;   // multiple of 8: token groups of one tile share an XCD
-    hipLaunchKernelGGL((gemm_kernel<MODE, NT>), dim3(gx, nz), dim3(256), lds_bytes, s, p);
+    hipLaunchKernelGGL((gemm_kernel<MODE, NT>), dim3(n_wg), dim3(256), lds_bytes, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int nz,
+hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
                        hipStream_t s) {
     if (mode == 0) {
-        return tile_tokens == 32 ? launch_gemm_t<0, 1>(p, lds_bytes, nz, s)
-                                 : launch_gemm_t<0, 4>(p, lds_bytes, nz, s);
+        return tile_tokens == 32 ? launch_gemm_t<0, 1>(p, lds_bytes, n_wg, s)
+                                 : launch_gemm_t<0, 4>(p, lds_bytes, n_wg, s);
     }
-    return tile_tokens == 32 ? launch_gemm_t<1, 1>(p, lds_bytes, nz, s)
-                             : launch_gemm_t<1, 4>(p, lds_bytes, nz, s);
+    return tile_tokens == 32 ? launch_gemm_t<1, 1>(p, lds_bytes, n_wg, s)
+                             : launch_gemm_t<1, 4>(p, lds_bytes, n_wg, s);
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,

@@ -71,11 +71,9 @@ class PagedMoELayer:
         s = stream if stream is not None else torch.cuda.current_stream()
         return B.pw_layer_status(self.handle, int(s.cuda_stream))
 
-    def set_profiling(self, enable: bool) -> None:
-        B.pw_layer_set_profiling(self.handle, enable)
-
-    def get_profile(self):
-        return B.pw_layer_get_profile(self.handle)
+    def replay(self, phase: int, stream: Optional[torch.cuda.Stream] = None) -> None:
+        s = stream if stream is not None else torch.cuda.current_stream()
+        B.pw_moe_replay(self.handle, phase, int(s.cuda_stream))
 
     def last_bytes(self, stream: Optional[torch.cuda.Stream] = None):
         s = stream if stream is not None else torch.cuda.current_stream()

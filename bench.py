@@ -38,6 +38,8 @@ def main():
     ap.add_argument("--clones", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -47,9 +49,19 @@ def main():
     import torch
 
     import synth
-    from any_precision_bit_amd import PagedMoELayer, route_buffers
+    from any_precision_bit_amd import PagedMoELayer
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB x 5 (reads and writes {n} bytes per copy)")
+        return
     cfg = synth.CONFIGS["c1"]
     T = cfg.T
     t0 = time.time()
@@ -88,11 +100,9 @@ def main():
         c = clones[i % len(clones)]
         c["lay"].forward(x, c["wr"], None, y=c["y"], stream=stream)
     torch.cuda.synchronize()
-    for c in clones:
-        c["lay"].set_profiling(True)
 
+    # headline: whole forwards back to back, events only around the timed region
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
@@ -104,23 +114,29 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
 
-    # per-kernel durations from the library's events on the forward's stream
-    n_calls, ms_k = 0, [0.0] * 4
-    for c in clones:
-        n, ms = c["lay"].get_profile()
-        n_calls += n
-        ms_k = [a + b for a, b in zip(ms_k, ms)]
-        c["lay"].set_profiling(False)
-    avg_ms = [m / max(1, n_calls) for m in ms_k]
+    # per-phase durations: each phase of the last forward of every clone replayed
+    # back to back over the same rotation, HIP events on the launch stream around it
+    ran = min(len(clones), max(args.warmup, args.steps))   # clones that have run a forward
+    n_rep = max(args.steps // 2, ran)
+    avg_ms = []
+    for phase in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_rep):
+            clones[i % ran]["lay"].replay(phase, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_ms.append(e0.elapsed_time(e1) / n_rep)
     nbytes = clones[0]["lay"].last_bytes(stream)
-    names = ["route", "gate_up", "down", "residual"]
+    names = ["routing", "gate_up", "down"]
     for i in range(3):
         gbs = nbytes[i] / (avg_ms[i] * 1e-3) / 1e9 if avg_ms[i] > 0 else 0.0
         log(f"  {names[i]:8s} {avg_ms[i] * 1e3:8.2f} us  {nbytes[i] / 1e6:8.2f} MB  {gbs:8.1f} GB/s")
     layer_bytes = nbytes[0] + nbytes[1] + nbytes[2]
     layer_gbs = layer_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.2f} us, layer bytes {layer_bytes / 1e6:.1f} MB -> {layer_gbs:.0f} GB/s "
-        f"({layer_gbs / HBM_PEAK_GBS:.1%} of HBM peak); wall {wall:.3f}s")
+    log(f"step {ms_per_step * 1e3:.2f} us (phases sum {sum(avg_ms) * 1e3:.2f} us), layer bytes "
+        f"{layer_bytes / 1e6:.1f} MB -> {layer_gbs:.0f} GB/s ({layer_gbs / HBM_PEAK_GBS:.1%} of HBM peak); "
+        f"wall {wall:.3f}s")
 
     # dominant kernel: gate_up (about two thirds of the layer's bytes)
     gu_gbs = nbytes[1] / (avg_ms[1] * 1e-3) / 1e9

@@ -69,13 +69,14 @@ typedef struct pw_layer_s* pw_layer;  /* opaque; one MoE layer */
 
 typedef struct {
     int32_t abi_version;   /* PW_ABI_VERSION */
-    int32_t d_model;       /* d: hidden size, multiple of 128 */
+    int32_t d_model;       /* d: hidden size, multiple of 128, at most 8192 */
     int32_t n_experts;     /* E routed experts, 1..PW_MAX_EXPERTS */
     int32_t d_ffn;         /* F: routed expert ffn size, multiple of 128 */
     int32_t top_k;         /* k, 1..min(E, PW_MAX_TOP_K) */
     int32_t d_ffn_shared;  /* F_s: shared expert ffn size, 0 = none, else multiple of 128;
                               the shared expert has expert id E */
-    int32_t max_tokens;    /* upper bound on T per forward, 1..65536 */
+    int32_t max_tokens;    /* upper bound on T per forward, 1..65536, with
+                              max_tokens*(top_k+1)*max(d_ffn, d_ffn_shared) < 2^31 */
     uint32_t flags;        /* must be 0 */
 } pw_moe_desc;
 
@@ -143,14 +144,13 @@ pw_status pw_moe_forward(pw_layer layer, const void* x, int32_t T, const void* r
  * *flags (PW_STATUS_* bits). Returns PW_E_STATE if any flag was set. */
 pw_status pw_layer_status(pw_layer layer, void* stream, uint32_t* flags);
 
-/* Per-kernel timing with HIP events recorded on the forward's stream between
- * its kernels. Enabling clears the accumulated times. */
-pw_status pw_layer_set_profiling(pw_layer layer, int32_t enable);
-
-/* Synchronises the recorded events and returns, over the forwards since
- * profiling was enabled, the call count and the summed milliseconds of each
- * kernel: ms[0] route, ms[1] gate_up, ms[2] down, ms[3] residual. */
-pw_status pw_layer_get_profile(pw_layer layer, int32_t* n_calls, float* ms /*[4]*/);
+/* Measurement hook: enqueues again, on `stream`, the kernels of one phase of
+ * this layer's last forward with the same arguments: 0 routing (router + bucket
+ * sort), 1 gate_up + SwiGLU, 2 down + weighted accumulation, 3 residual. Used to
+ * time one phase alone; the buffers of that forward must still be alive. The
+ * phase rewrites its outputs (phase 0 zeroes y, phase 2 adds into y again), so
+ * y is meaningful only after a full forward. PW_E_STATE before any forward. */
+pw_status pw_moe_replay(pw_layer layer, int32_t phase, void* stream);
 
 /* Algorithmic bytes of the last forward's kernels, computed on the host from
  * the routed counts of that forward (reads them back; synchronises `stream`):

@@ -24,7 +24,7 @@ def B():
 
 def test_exports_every_declared_symbol(B):
     names = declared_functions()
-    assert len(names) >= 12
+    assert len(names) >= 11
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +35,7 @@ def test_create_validation(B):
     ok = dict(d_model=256, n_experts=8, d_ffn=512, top_k=2, d_ffn_shared=0, max_tokens=16)
     h = B.pw_layer_create(**ok)
     B.pw_layer_destroy(h)
-    bad = [dict(d_model=200), dict(d_model=0), dict(n_experts=0), dict(n_experts=257),
+    bad = [dict(d_model=200), dict(d_model=0), dict(d_model=8320), dict(n_experts=0), dict(n_experts=257),
            dict(d_ffn=100), dict(top_k=0), dict(top_k=9), dict(d_ffn_shared=-128),
            dict(d_ffn_shared=100), dict(max_tokens=0), dict(max_tokens=70000)]
     for b in bad:
@@ -141,13 +141,13 @@ def test_debug_hook_validation(B):
     assert ei.value.status == 5
 
 
-def test_status_and_profile_without_device_state(B):
+def test_status_and_replay_without_device_state(B):
     h = B.pw_layer_create(256, 8, 512, 2, 0, 16)
     try:
         assert B.pw_layer_status(h) == 0            # nothing allocated yet: flags 0
-        B.pw_layer_set_profiling(h, True)
-        n, ms = B.pw_layer_get_profile(h)
-        assert n == 0 and ms == [0.0] * 4
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_replay(h, 1)
+        assert ei.value.status == 7
         with pytest.raises(B.PwError) as ei:
             B.pw_layer_last_bytes(h)
         assert ei.value.status == 7
