@@ -145,6 +145,8 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_cnt = off;    off += al(sizeof(int32_t) * (size_t)E);
     const size_t o_off = off;    off += al(sizeof(int32_t) * ((size_t)E + 1));
     const size_t o_srt = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    const size_t o_stk = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    const size_t o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
     const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
     const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
@@ -171,6 +173,8 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.counts = (int32_t*)(b + o_cnt);
     L->ws.offsets = (int32_t*)(b + o_off);
     L->ws.sorted = (int32_t*)(b + o_srt);
+    L->ws.slot_tok = (int32_t*)(b + o_stk);
+    L->ws.slot_w = (float*)(b + o_sw);
     L->ws.prefix = (int32_t*)(b + o_pre);
     L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
@@ -214,13 +218,6 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
     L->stage_i = (slot + 1) % kStageSlots;
     L->dirty = false;
     return PW_OK;
-}
-
-int plan_bmax(const pw_layer_s* L, int lin_lo, int lin_hi) {
-    int bm = 1;
-    for (int e = 0; e < L->n_total; ++e)
-        for (int l = lin_lo; l <= lin_hi; ++l) bm = std::max(bm, (int)L->bits[e * 3 + l]);
-    return bm;
 }
 
 
@@ -409,9 +406,9 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     bp.E = E;
     bp.k = k;
     bp.has_shared = has_shared;
-    bp.tiles_gu_r = D.d_ffn / 64;
-    bp.tiles_gu_s = D.d_ffn_shared / 64;
-    bp.tiles_dn = d / 128;
+    bp.tiles_gu_r = D.d_ffn / 32;
+    bp.tiles_gu_s = D.d_ffn_shared / 32;
+    bp.tiles_dn = d / 64;
     bp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
     bp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
     bp.ws = L->ws;
@@ -435,20 +432,18 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     gp.ld_act = L->f_max;
     gp.shared_base = D.max_tokens * k;
     gp.y = y;
-    // gate_up + SwiGLU: items of 64 rows of F
-    L->lds_gu = pw::gemm_lds_bytes(plan_bmax(L, PW_GATE, PW_UP));
+    // gate_up + SwiGLU: items of 32 rows of F (gate and up)
+    L->lds_gu = pw::gemm_lds_bytes();
     L->gp_gu = gp;
-    L->gp_gu.lds_stripe = L->lds_gu - pw::kTokInfoBytes - (PW_MAX_EXPERTS + 2) * 4 - 16;
-    L->gp_gu.tiles_r = D.d_ffn / 64;
-    L->gp_gu.tiles_s = D.d_ffn_shared / 64;
+    L->gp_gu.tiles_r = D.d_ffn / 32;
+    L->gp_gu.tiles_s = D.d_ffn_shared / 32;
     L->gp_gu.pieces_r = L->gp_gu.pieces_s = 1;
     L->gp_gu.b_bytes = (uint32_t)((size_t)D.max_tokens * d * 2);
-    // down + weighted scatter-accumulate: items of 128 rows of d
-    L->lds_dn = pw::gemm_lds_bytes(plan_bmax(L, PW_DOWN, PW_DOWN));
+    // down + weighted scatter-accumulate: items of 64 rows of d
+    L->lds_dn = pw::gemm_lds_bytes();
     L->gp_dn = gp;
-    L->gp_dn.lds_stripe = L->lds_dn - pw::kTokInfoBytes - (PW_MAX_EXPERTS + 2) * 4 - 16;
-    L->gp_dn.tiles_r = d / 128;
-    L->gp_dn.tiles_s = has_shared ? d / 128 : 0;
+    L->gp_dn.tiles_r = d / 64;
+    L->gp_dn.tiles_s = has_shared ? d / 64 : 0;
     L->gp_dn.pieces_r = bp.pieces_dn_r;
     L->gp_dn.pieces_s = has_shared ? bp.pieces_dn_s : 1;
     L->gp_dn.b_bytes = (uint32_t)(((size_t)D.max_tokens * k + (size_t)D.max_tokens * has_shared) * L->f_max * 2);

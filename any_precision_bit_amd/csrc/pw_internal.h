@@ -30,6 +30,8 @@ struct Workspace {
     int32_t* counts;     // [E]
     int32_t* offsets;    // [E+1]
     int32_t* sorted;     // [max_T*k]    assignment t*k+j, grouped by expert
+    int32_t* slot_tok;   // [max_T*k]    token t of each sorted slot
+    float* slot_w;       // [max_T*k]    routing weight of each sorted slot
     int32_t* prefix;     // [N_LISTS][E+2]
     uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
@@ -58,13 +60,14 @@ struct BucketParams {
     int32_t* o_sorted;
 };
 
-// Dequantising GEMM over (expert, row tile, token group) items of one list.
-// An item covers 64 rows of each of two row-sets; wave w of the work-group
-// owns row block (w >> 1) (32 rows) and K-half (w & 1).
-// gate_up: set 0 = gate rows [f0, f0+64), set 1 = up rows [f0, f0+64), K = d,
+// Dequantising GEMM over (expert, row tile, K-piece, token group) items of one
+// list. An item covers 32 rows of each of two row-sets; wave w of the
+// work-group owns the 256-column chunks w, w+4, ... of the item's K range.
+// gate_up: set 0 = gate rows [f0, f0+32), set 1 = up rows [f0, f0+32), K = d,
 //          B = xperm rows (tokens), epilogue SwiGLU -> act (fp16).
-// down:    set 0 = rows [r0, r0+64), set 1 = rows [r0+64, r0+128), K = F,
-//          B = act rows (slots), epilogue w * o atomically added to y (fp32).
+// down:    set 0 = rows [r0, r0+32), set 1 = rows [r0+32, r0+64), K = F (in
+//          pieces of kDownPiece columns), B = act rows (slots), epilogue
+//          w * o atomically added to y (fp32).
 struct GemmParams {
     const DevBlock* blocks;   // [n_total*3]
     int E, k, T, d;
@@ -76,7 +79,6 @@ struct GemmParams {
     Workspace ws;
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
-    int lds_stripe;           // LDS bytes reserved for the LUT stripe / reduction
     uint32_t b_bytes;         // size of the B-operand buffer (xperm or act)
     float* y;
 };
@@ -92,10 +94,9 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, 
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
-// LDS bytes of the gemm kernels for a largest bitwidth bmax.
-int gemm_lds_bytes(int bmax);
+// LDS bytes of the gemm kernels.
+int gemm_lds_bytes();
 
-constexpr int kTokInfoBytes = 128 * 12;   // per-item token rows / outputs / weights
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
 constexpr int kRouteThreads = 512;
 constexpr int kBucketThreads = 1024;

@@ -73,6 +73,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Loads of wave-uniform addresses from data the kernel does not write (page
+// table, routing counts and offsets of an earlier kernel) go through the
+// constant address space, so they are scalar loads served by the scalar cache.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* kconst(const T* p) {
+    return (const __attribute__((address_space(4))) T*)(size_t)p;
+}
+
 // Position of column c (0..31) of a 32-column group in the permuted activation
 // layout: column 8k + i goes to 8*(i>>1) + 2k + (i&1). Eight consecutive
 // permuted positions 8m..8m+7 are the columns one MFMA step m consumes.
@@ -445,6 +453,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketParams p) 
         if (valid) {
             const int pos = s_wc[wave * E + e] + rank;
             p.ws.sorted[pos] = i;
+            p.ws.slot_tok[pos] = i / p.k;   // token of the slot, and its routing weight
+            p.ws.slot_w[pos] = p.ws.w[i];
             if (p.o_sorted) p.o_sorted[pos] = i;
         }
         __syncthreads();
@@ -525,52 +535,66 @@ __device__ __forceinline__ half8 lut_fragment(const uint32_t (&rw)[8], int m, ui
 }
 
 // 8 LUT entries [c8, c8+8) of one row as four packed fp16 pairs (zeros past 2^b).
+// A row of b < 3 is 4 or 8 bytes; it is read whole (c8 is 0 then).
 __device__ __forceinline__ uint4 load_lut8(const uint16_t* row, int b, int c8) {
-    const int n = 1 << b;
-    if (b >= 3) return c8 < n ? *(const uint4*)(row + c8) : make_uint4(0, 0, 0, 0);
-    uint32_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (c8 + i < n) ? row[c8 + i] : 0u;
-    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+    if (b >= 3) return c8 < (1 << b) ? *(const uint4*)(row + c8) : make_uint4(0, 0, 0, 0);
+    if (b == 2) {
+        const uint2 v = *(const uint2*)row;
+        return make_uint4(v.x, v.y, 0, 0);
+    }
+    return make_uint4(*(const uint32_t*)row, 0, 0, 0);
 }
 
 // Writes 8 consecutive stripe entries (idx = c8..c8+7) of one row slot:
-// dword (idx*64 + row) = {set0 LUT[row][idx], set1 LUT[row][idx]}.
+// dword (idx*64 + row) = {set0 LUT[row][idx], set1 LUT[row][idx]}. One base
+// address, the entries at fixed offsets of 256 bytes.
 __device__ __forceinline__ void write_stripe8(uint32_t* stripe, int c8, int row, int nidx, uint4 a, uint4 b) {
+    uint32_t* dst = stripe + c8 * 64 + row;
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    if (nidx >= 8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = c8 + 2 * i;
-        if (idx < nidx) stripe[idx * 64 + row] = (av[i] & 0xFFFFu) | (bv[i] << 16);
-        if (idx + 1 < nidx) stripe[(idx + 1) * 64 + row] = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
+        for (int i = 0; i < 4; ++i) {
+            dst[(2 * i) * 64] = (av[i] & 0xFFFFu) | (bv[i] << 16);
+            dst[(2 * i + 1) * 64] = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (2 * i < nidx) dst[(2 * i) * 64] = (av[i] & 0xFFFFu) | (bv[i] << 16);
+            if (2 * i + 1 < nidx) dst[(2 * i + 1) * 64] = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
+        }
     }
 }
 
-// Stages the LUTs of 64 rows of both row-sets into the LDS stripe. Loads are
-// issued in rounds of 4 per thread and set before their LDS writes: one memory
-// round trip for b <= 7, two for b = 8.
-__device__ __forceinline__ void stage_luts64(uint32_t* stripe, const uint16_t* lut0, int b0,
-                                             const uint16_t* lut1, int b1, int tid) {
-    constexpr int RIT = 4;
-    const int bmax = b0 > b1 ? b0 : b1;
-    const int nidx = 1 << bmax;
-    const int total = (nidx >= 8 ? nidx / 8 : 1) * 64;
-    for (int base = 0; base < total; base += RIT * 256) {
-        uint4 v0[RIT], v1[RIT];
+// LUT entries of an item's 32 rows of both row-sets, eight per load: unit j
+// covers row j & 31, entries 8*(j >> 5) .. +7. At most 4 units per thread (b = 8).
+// The loads are issued early (lut_stage_load) and written to the stripe later
+// (lut_stage_write), so their latency hides behind other work.
+struct LutStage {
+    uint4 v0[4], v1[4];
+};
+__device__ __forceinline__ int lut_units(int bmax) {
+    return ((1 << bmax) >= 8 ? (1 << bmax) / 8 : 1) * 32;
+}
+__device__ __forceinline__ void lut_stage_load(LutStage& st, const uint16_t* lut0, int b0,
+                                               const uint16_t* lut1, int b1, int tid) {
+    const int total = lut_units(b0 > b1 ? b0 : b1);
 #pragma unroll
-        for (int it = 0; it < RIT; ++it) {
-            const int j = base + tid + it * 256;
-            if (j < total) {
-                const int r = j & 63, c8 = (j >> 6) * 8;
-                v0[it] = load_lut8(lut0 + ((size_t)r << b0), b0, c8);
-                v1[it] = load_lut8(lut1 + ((size_t)r << b1), b1, c8);
-            }
+    for (int it = 0; it < 4; ++it) {
+        const int j = tid + it * 256;
+        if (j < total) {
+            const int r = j & 31, c8 = (j >> 5) * 8;
+            st.v0[it] = load_lut8(lut0 + ((size_t)r << b0), b0, c8);
+            st.v1[it] = load_lut8(lut1 + ((size_t)r << b1), b1, c8);
         }
+    }
+}
+__device__ __forceinline__ void lut_stage_write(uint32_t* stripe, const LutStage& st, int bmax, int tid) {
+    const int total = lut_units(bmax);
 #pragma unroll
-        for (int it = 0; it < RIT; ++it) {
-            const int j = base + tid + it * 256;
-            if (j < total) write_stripe8(stripe, (j >> 6) * 8, j & 63, nidx, v0[it], v1[it]);
-        }
+    for (int it = 0; it < 4; ++it) {
+        const int j = tid + it * 256;
+        if (j < total) write_stripe8(stripe, (j >> 5) * 8, j & 31, 1 << bmax, st.v0[it], st.v1[it]);
     }
 }
 
@@ -597,8 +621,8 @@ struct Item {
     int K, R;                 // columns / rows of the block
     int kbase, klen;          // K range of this item
     int rows0, rows1;         // first row of set 0 / set 1
-    const DevBlock* blk0;
-    const DevBlock* blk1;
+    const __attribute__((address_space(4))) DevBlock* blk0;   // page-table entries (scalar loads)
+    const __attribute__((address_space(4))) DevBlock* blk1;
 };
 
 // Token rows of one item for thread tid (tid < nl): B row, output row, weight.
@@ -610,18 +634,19 @@ struct TokInfo {
 template <int MODE>
 __device__ __forceinline__ TokInfo fetch_tokinfo(const GemmParams& p, const Item& it, int tid) {
     TokInfo tk{0, 0, 0.0f};
+    const bool sh = it.ex == p.E;
+    const int base = sh ? 0 : kconst(p.ws.offsets)[it.ex];
     if (tid < it.nl) {
-        const bool sh = it.ex == p.E;
         const int tkn = it.tbase + tid;
-        const int slot = sh ? (p.shared_base + tkn) : (p.ws.offsets[it.ex] + tkn);
+        const int slot = sh ? (p.shared_base + tkn) : (base + tkn);
+        const int tok = sh ? tkn : p.ws.slot_tok[slot];
         if (MODE == 0) {
-            tk.brow = sh ? tkn : p.ws.sorted[slot] / p.k;   // token: xperm row
-            tk.orow = slot;                                 // act row
+            tk.brow = tok;    // xperm row
+            tk.orow = slot;   // act row
         } else {
-            const int asg = sh ? 0 : p.ws.sorted[slot];
-            tk.brow = slot;                                 // act row
-            tk.orow = sh ? tkn : asg / p.k;                 // token: y row
-            tk.w = sh ? 1.0f : p.ws.w[asg];
+            tk.brow = slot;   // act row
+            tk.orow = tok;    // y row
+            tk.w = sh ? 1.0f : p.ws.slot_w[slot];
         }
     }
     return tk;
@@ -644,43 +669,59 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     it.tile = local % tiles;
     const int piece = (local / tiles) % pieces;
     it.grp = local / tiles / pieces;
-    it.n_tok = sh ? p.T : p.ws.counts[it.ex];
+    it.n_tok = sh ? p.T : kconst(p.ws.counts)[it.ex];
     it.tbase = it.grp * 32 * NT;
     it.nl = min(32 * NT, it.n_tok - it.tbase);
     if (MODE == 0) {
         it.K = p.d;
         it.R = sh ? p.Fs : p.F;
-        it.rows0 = it.rows1 = it.tile * 64;
-        it.blk0 = &p.blocks[it.ex * 3 + 0];
-        it.blk1 = &p.blocks[it.ex * 3 + 1];
+        it.rows0 = it.rows1 = it.tile * 32;
+        it.blk0 = kconst(p.blocks) + it.ex * 3 + 0;
+        it.blk1 = kconst(p.blocks) + it.ex * 3 + 1;
     } else {
         it.K = sh ? p.Fs : p.F;
         it.R = p.d;
-        it.rows0 = it.tile * 128;
-        it.rows1 = it.tile * 128 + 64;
-        it.blk0 = it.blk1 = &p.blocks[it.ex * 3 + 2];
+        it.rows0 = it.tile * 64;
+        it.rows1 = it.tile * 64 + 32;
+        it.blk0 = it.blk1 = kconst(p.blocks) + it.ex * 3 + 2;
     }
     it.kbase = piece * kDownPiece;
     it.klen = min(it.K - it.kbase, MODE == 0 ? it.K : kDownPiece);
     return it;
 }
 
-// Persistent work-group of 4 waves over the items of one list. Wave w owns row
-// block rb = w >> 1 (32 rows of each set) and K-half kh = w & 1 (256-column
-// chunks kh, kh+2, ...). MODE 0: gate_up, MODE 1: down. NT: token tiles of 32.
+// LDS of the gemm kernels: a 64 KiB stripe whose 256-byte row idx holds, in
+// dwords 0..31, the LUT entry idx of the item's 32 row slots (low half: set 0,
+// high half: set 1) and, in dwords 32..63, the cross-wave reduction buffer;
+// then the token rows of two items (double buffer), the work-list prefix and
+// the item hand-over words.
+constexpr int kStripeBytes = 65536;
+constexpr int kTokWords = 3 * 128;   // brow, orow, weight bits of up to 128 tokens
+
+// Persistent work-group of 4 waves over the items of one list. An item is 32
+// rows of each of two row-sets over the item's K range; wave q owns the
+// 256-column chunks q, q+4, q+8, ... Lane (r, g) of each wave reads 16 bytes of
+// row r per plane and chunk, so for every 128-byte line of a plane row the four
+// waves read its four 32-byte quarters together and the line is fetched from
+// HBM once. The four partial sums meet in LDS; wave q finishes accumulator
+// registers 4q..4q+3 (rows 8q..8q+7 of the 32x32 tile).
+// MODE 0: gate_up, MODE 1: down. NT: token tiles of 32.
 template <int MODE, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 31, g = lane >> 5, rb = wave >> 1, kh = wave & 1;
-    int* s_brow = (int*)(smem + p.lds_stripe);
-    int* s_orow = s_brow + 128;
-    float* s_ow = (float*)(s_orow + 128);
-    int* s_pre = (int*)(smem + p.lds_stripe + kTokInfoBytes);
-    int* s_item = s_pre + PW_MAX_EXPERTS + 2;   // [0] first item, [1] reserved next item
+    // tid, r and g are re-declared opaque at every item (below) so that the
+    // compiler recomputes values derived from them instead of keeping dozens of
+    // them live across the persistent loop
+    int tid = threadIdx.x;
+    const int q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
+    int r = tid & 31, g = (tid >> 5) & 1;
+    uint32_t* stripe = (uint32_t*)smem;
+    int* s_tok = (int*)(smem + kStripeBytes);           // [2][kTokWords]
+    int* s_pre = s_tok + 2 * kTokWords;
+    int* s_item = s_pre + PW_MAX_EXPERTS + 2;           // [0] first item, [1] reserved next item
     const int npos = p.E + p.has_shared;
     // Items are handed out by an atomic counter; each work-group holds one item in
-    // reserve so that its first chunk can be prefetched. The last work-group to
+    // reserve so that its first chunks can be prefetched. The last work-group to
     // leave resets the counters for the next launch.
     uint32_t* cnt = p.ws.sched + 2 * p.list;
     auto leave = [&]() {
@@ -699,52 +740,69 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         return;
     }
 
-    const uint32_t slot = lds_addr(smem) + (uint32_t)((rb * 32 + r) * 4);
     const uint16_t* Bbase = MODE == 0 ? p.ws.xperm : p.ws.act;
     const int ldb = MODE == 0 ? p.d : p.ld_act;
     const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(Bbase, p.b_bytes);
 
+    // reduction slot of (wave w, set s, accumulator register v) of this lane
+    auto red = [&](int w, int s, int v) -> float* {
+        return (float*)&stripe[((((w * 2 + s) * 16 + v) * 2 + g) << 6) + 32 + r];
+    };
+
     uint4 pa0[8], pa1[8], pb0[8], pb1[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) pa0[q] = pa1[q] = pb0[q] = pb1[q] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) pa0[i] = pa1[i] = pb0[i] = pb1[i] = make_uint4(0, 0, 0, 0);
 
-    // plane loads of chunk ch of an item into (c0, c1); lanes past K load nothing
-    // plane loads of chunk ch of an item into (c0, c1): slot q holds plane
-    // q - (8 - b); slots below 8 - b and lanes past K read zeros
+    // plane loads of chunk ch of an item into (c0, c1): slot i holds plane
+    // i - (8 - b); slots below 8 - b and lanes past the item's K range read zeros
     auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
         const int Kb = it.K >> 3;
         const bool vg = (ch * 256 + g * 128) < it.klen;
         const uint32_t nrec = (uint32_t)(it.R * Kb);
-        const int cb = (it.kbase >> 3) + g * 16 + ch * 32;
-        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + rb * 32 + r) * Kb + cb) : kOOB;
-        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + rb * 32 + r) * Kb + cb) : kOOB;
+        const int cb = (it.kbase >> 3) + ch * 32 + g * 16;
+        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + r) * Kb + cb) : kOOB;
+        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + r) * Kb + cb) : kOOB;
         const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            c0[q] = buf_load16(make_rsrc((const void*)it.blk0->planes[q], q >= s0 ? nrec : 0u), off0);
-            c1[q] = buf_load16(make_rsrc((const void*)it.blk1->planes[q], q >= s1 ? nrec : 0u), off1);
+        for (int i = 0; i < 8; ++i) {
+            c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
+            c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
         }
+    };
+    auto n_chunks = [](const Item& it) { return (it.klen + 255) >> 8; };
+    auto start_item = [&](const Item& it, LutStage& st, TokInfo& tk) {
+        if (q < n_chunks(it)) load_chunk(it, q, pa0, pa1);
+        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
+        lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
+                       (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
+        tk = fetch_tokinfo<MODE>(p, it, tid);
+    };
+    auto publish_item = [&](const Item& it, const LutStage& st, const TokInfo& tk, int par) {
+        if (tid < it.nl) {
+            int* tb = s_tok + par * kTokWords;
+            tb[tid] = tk.brow;
+            tb[128 + tid] = tk.orow;
+            tb[256 + tid] = __float_as_int(tk.w);
+        }
+        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
+        lut_stage_write(stripe, st, b0 > b1 ? b0 : b1, tid);
     };
 
     Item it = decode_item<MODE, NT>(p, s_pre, npos, item);
-    if (kh < ((it.klen + 255) >> 8)) load_chunk(it, kh, pa0, pa1);
-    TokInfo tk = fetch_tokinfo<MODE>(p, it, tid);
+    {
+        LutStage st;
+        TokInfo tk;
+        start_item(it, st, tk);
+        publish_item(it, st, tk, 0);
+    }
+    __syncthreads();
+    int par = 0;
 
     while (true) {
-        const int nch = (it.klen + 255) >> 8;
-        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
-        const bool sh = it.ex == p.E;
+        asm volatile("" : "+v"(tid), "+v"(r), "+v"(g));
+        const int nch = n_chunks(it);
         const int ntl = (it.nl + 31) >> 5;
-        __syncthreads();   // the previous item's epilogue is done with LDS
-        int grab = 0;   // next item, reserved during this wave's last chunk
-        if (tid < it.nl) {
-            s_brow[tid] = tk.brow;
-            s_orow[tid] = tk.orow;
-            s_ow[tid] = tk.w;
-        }
-        stage_luts64((uint32_t*)smem, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
-                     (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
-        __syncthreads();
+        const int* tb = s_tok + par * kTokWords;
 
         uint32_t boff[NT];
         bool bok[NT];
@@ -752,7 +810,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         for (int nt = 0; nt < NT; ++nt) {
             const int i = nt * 32 + r;
             bok[nt] = i < it.nl;
-            boff[nt] = bok[nt] ? (uint32_t)(s_brow[i] * ldb + g * 128) : 0u;
+            boff[nt] = bok[nt] ? (uint32_t)(tb[i] * ldb + g * 128) : 0u;
         }
         floatx16 acc0[NT], acc1[NT];
 #pragma unroll
@@ -764,7 +822,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         auto load_b = [&](int ch, int dw, half8 (&bf)[NT][4], bool vg) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const uint32_t off = (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 256 + 32 * dw)) * 2u : kOOB;
+                const uint32_t off =
+                    (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 256 + 32 * dw)) * 2u : kOOB;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) bf[nt][m] = __builtin_bit_cast(half8, buf_load16(brsrc, off + 16u * m));
             }
@@ -772,21 +831,21 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
 
         // One 256-column chunk: for each of the four 32-column dwords, transpose the
         // plane words of both sets, look the weights up and feed the MFMAs. The B
-        // fragments of dword dw+1 load while dword dw computes (two named buffers,
-        // the dword loop is unrolled). Lanes past K hold zero B fragments, so their
-        // A fragments need no masking.
+        // fragments of a dword (L2-resident activations) load at its start and
+        // arrive while the transposes and lookups run. Lanes past K hold zero B
+        // fragments, so their A fragments need no masking.
+        const uint32_t slot = lds_addr(smem) + (uint32_t)(r * 4);
         auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
             const bool vg = (ch * 256 + g * 128) < it.klen;
             half8 bfr[2][NT][4];
-            load_b(ch, 0, bfr[0], vg);
 #pragma unroll
             for (int dw = 0; dw < 4; ++dw) {
-                if (dw < 3) load_b(ch, dw + 1, bfr[(dw + 1) & 1], vg);
+                load_b(ch, dw, bfr[dw & 1], vg);
                 uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    w0[q] = word_of(c0[q], dw);
-                    w1[q] = word_of(c1[q], dw);
+                for (int i = 0; i < 8; ++i) {
+                    w0[i] = word_of(c0[i], dw);
+                    w1[i] = word_of(c1[i], dw);
                 }
                 slots_to_indices(w0, rw0);
                 slots_to_indices(w1, rw1);
@@ -805,70 +864,91 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
             }
         };
 
-        // ping-pong over this wave's chunks kh, kh+2, ...: chunk in A while the next loads into B
-        if (kh >= nch && tid == 0) grab = (int)atomicAdd(cnt, 1u);
-        for (int ch = kh; ch < nch; ch += 4) {
-            if (ch + 2 < nch) load_chunk(it, ch + 2, pb0, pb1);
-            else if (tid == 0) grab = (int)atomicAdd(cnt, 1u);
+        // this wave's chunks q, q+4, ...: the first arrives in pa (prefetched with
+        // the item), later ones load into a buffer as soon as it has been
+        // consumed. Wave 0 reserves the next item when it starts on its last chunk.
+        int grab = 0;
+        if (q + 4 < nch) load_chunk(it, q + 4, pb0, pb1);
+#pragma unroll 1
+        for (int ch = q; ch < nch; ch += 8) {
+            if (tid == 0 && ch + 4 >= nch) grab = (int)atomicAdd(cnt, 1u);
             compute_chunk(ch, pa0, pa1);
-            if (ch + 2 >= nch) break;
-            if (ch + 4 < nch) load_chunk(it, ch + 4, pa0, pa1);
-            else if (tid == 0) grab = (int)atomicAdd(cnt, 1u);
-            compute_chunk(ch + 2, pb0, pb1);
+            if (ch + 8 < nch) load_chunk(it, ch + 8, pa0, pa1);
+            if (ch + 4 >= nch) break;
+            if (tid == 0 && ch + 8 >= nch) grab = (int)atomicAdd(cnt, 1u);
+            compute_chunk(ch + 4, pb0, pb1);
+            if (ch + 12 < nch) load_chunk(it, ch + 12, pb0, pb1);
         }
 
-        // next item: decode and start its first chunk before this item's epilogue
+        // partial sums of token tile nt for the other waves' accumulator registers
+        auto put_partials = [&](int nt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if ((v >> 2) != q) {
+                    *red(q, 0, v) = acc0[nt][v];
+                    *red(q, 1, v) = acc1[nt][v];
+                }
+            }
+        };
+        // sum of the four partials of registers 4q..4q+3 and the epilogue for them
+        auto finish = [&](int nt) {
+            const int tok_i = nt * 32 + r;
+            const bool tv = tok_i < it.nl;
+            const int orow = tv ? tb[128 + tok_i] : 0;
+            const float wv = tv ? __int_as_float(tb[256 + tok_i]) : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if ((v >> 2) != q) continue;
+                float s0 = acc0[nt][v], s1 = acc1[nt][v];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if (w != q) {
+                        s0 += *red(w, 0, v);
+                        s1 += *red(w, 1, v);
+                    }
+                }
+                if (!tv) continue;
+                const int row = q * 8 + g * 4 + (v & 3);
+                if (MODE == 0) {
+                    const float av = s0 / (1.0f + expf(-s0)) * s1;
+                    const int f = it.rows0 + row;
+                    p.ws.act[(size_t)orow * p.ld_act + (f & ~31) + perm32(f & 31)] = f2h(av);
+                } else {
+                    float* yr = p.y + (size_t)orow * p.d;
+                    unsafeAtomicAdd(yr + it.rows0 + row, wv * s0);
+                    unsafeAtomicAdd(yr + it.rows1 + row, wv * s1);
+                }
+            }
+        };
+
+        put_partials(0);
         if (tid == 0) s_item[1] = grab;
-        __syncthreads();             // s_item[1] is visible; every wave is done with the LUT stripe
+        __syncthreads();   // every wave is done with the LUT slots; partials and s_item[1] visible
         const int next = __builtin_amdgcn_readfirstlane(s_item[1]);
+        const bool has_next = next < n_items;
         Item nit = it;
-        TokInfo ntk = tk;
-        if (next < n_items) {
+        LutStage st;
+        TokInfo ntk{0, 0, 0.0f};
+        if (has_next) {
             nit = decode_item<MODE, NT>(p, s_pre, npos, next);
-            if (kh < ((nit.klen + 255) >> 8)) load_chunk(nit, kh, pa0, pa1);
-            ntk = fetch_tokinfo<MODE>(p, nit, tid);
+            start_item(nit, st, ntk);
         }
-
-        // ---- K-half reduction through LDS (odd waves hand over), epilogue on even waves
-        float* red = (float*)smem;   // [rb][set][16][64]
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt >= ntl) break;
-            if (kh == 1) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    red[((rb * 2 + 0) * 16 + v) * 64 + lane] = acc0[nt][v];
-                    red[((rb * 2 + 1) * 16 + v) * 64 + lane] = acc1[nt][v];
-                }
+            if (nt > 0) {
+                __syncthreads();   // tile nt-1's partials have been read
+                put_partials(nt);
+                __syncthreads();
             }
-            __syncthreads();
-            if (kh == 0) {
-                const int tok_i = nt * 32 + r;
-                if (tok_i < it.nl) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float s0 = acc0[nt][v] + red[((rb * 2 + 0) * 16 + v) * 64 + lane];
-                        const float s1 = acc1[nt][v] + red[((rb * 2 + 1) * 16 + v) * 64 + lane];
-                        const int row = rb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-                        if (MODE == 0) {
-                            const float av = s0 / (1.0f + expf(-s0)) * s1;
-                            const int f = it.rows0 + row;
-                            p.ws.act[(size_t)s_orow[tok_i] * p.ld_act + (f & ~31) + perm32(f & 31)] = f2h(av);
-                        } else {
-                            const float wv = s_ow[tok_i];
-                            float* yr = p.y + (size_t)s_orow[tok_i] * p.d;
-                            unsafeAtomicAdd(yr + it.rows0 + row, wv * s0);
-                            unsafeAtomicAdd(yr + it.rows1 + row, wv * s1);
-                        }
-                    }
-                }
-            }
-            if (nt + 1 < ntl) __syncthreads();
+            finish(nt);
         }
-        if (next >= n_items) break;
+        if (has_next) publish_item(nit, st, ntk, par ^ 1);
+        __syncthreads();   // next item's LUT slots and token rows are in place; partials read
+        if (!has_next) break;
         item = next;
         it = nit;
-        tk = ntk;
+        par ^= 1;
     }
     leave();
 }
@@ -950,10 +1030,8 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
 
 // ============================================================================ launchers
 
-int gemm_lds_bytes(int bmax) {
-    const int stripe = 256 << bmax;
-    const int red = 2 * 2 * 16 * 64 * 4;
-    return (stripe > red ? stripe : red) + kTokInfoBytes + (PW_MAX_EXPERTS + 2) * 4 + 16;
+int gemm_lds_bytes() {
+    return kStripeBytes + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4 + 2 * 4;
 }
 
 hipError_t launch_init_ws(const Workspace& ws, hipStream_t s) {
