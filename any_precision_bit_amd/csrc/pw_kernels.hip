@@ -6,25 +6,28 @@
 // and fuses routing, SwiGLU expert activation and weighted accumulation.
 //
 // Kernels, in stream order per forward:
-//   route_kernel   exact router logits (int64, units of 2^-48), top-k softmax per
-//                  token (last-arriving workgroup of the token), then a stable
-//                  token->expert bucket sort (last-arriving workgroup of the call);
-//                  also writes the column-permuted copy of x and zeroes y.
-//   gemm_kernel<0> gate and up of each (expert, 32-row tile, token group):
+//   route_kernel   one work-group per token: fp32 router logits with an error
+//                  bound, exact int64 logits (units of 2^-48) for the candidates
+//                  the bound cannot rule out, exact top-k, softmax over the k
+//                  selected; also the column-permuted copy of x, and y = 0.
+//   bucket_kernel  one work-group: per-expert counts and offsets, the stable
+//                  token->expert order, each slot's token and weight, and the
+//                  per-expert work-item prefixes of the gemm lists.
+//   gemm_kernel<0> gate and up of (expert, 32-row tile, token group) items:
 //                  bit-plane unpack + LUT dequant into MFMA A fragments, MFMA
 //                  32x32x16 fp16 with fp32 accumulation, SwiGLU -> act (fp16).
-//   gemm_kernel<1> down of each (expert, 64-row tile, token group), scaled by
-//                  the routing weight and atomically added into y (fp32).
+//   gemm_kernel<1> down of (expert, 64-row tile, K-piece, token group) items,
+//                  scaled by the routing weight and atomically added into y.
 //   residual_kernel  x_next = fp16_rne(x + y) when requested.
 //
 // Dequantisation (the hot loop). Lane (r, g) of a wave owns row r (0..31) of the
-// tile and a 128-column half g of each 256-column chunk. For one 32-column dword
+// item and a 128-column half g of each 256-column chunk. For one 32-column dword
 // of each of the b planes, a three-stage bit-matrix transpose (8x8 per byte)
 // turns the b plane words into eight index words W_i whose byte k is the b-bit
 // index of column 8k+i. One v_perm per weight drops that byte into an LDS
 // address, and one 16-bit LDS read fetches the fp16 weight from the LUT stripe:
-// dword (idx*64 + g*32 + r) holds the two row-sets' LUT entries (low/high half),
-// so the 64 lanes of a wave always hit 64 distinct banks. Eight looked-up
+// dword (idx*64 + r) holds the two row-sets' LUT entries of row r (low/high
+// half), so each half-wave of 32 lanes hits 32 distinct banks. Eight looked-up
 // weights form one MFMA A operand; the B operand (activations) is stored with
 // the same in-group column permutation, so the contraction is unchanged.
 #include <hip/hip_runtime.h>

@@ -30,6 +30,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SRC = os.path.join(ROOT, "any_precision_bit_amd", "csrc", "pw_kernels.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_gate_up_c1_decode_traffic.md")
+
+
+def kernel_code_digest():
+    """sha256 of the kernel source with // comments and blank lines removed."""
+    import hashlib
+    code = [ln.split("//", 1)[0].rstrip() for ln in open(KERNEL_SRC)]
+    return hashlib.sha256("\n".join(c for c in code if c).encode()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a 1 GiB copy's readings), or None
+    when the kernel code has changed since those counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("kernel_code_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("kernel_code_sha256", "").strip() != kernel_code_digest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +167,7 @@ def main():
     gu_gbs = nbytes[1] / (avg_ms[1] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "gemm_kernel<0,1> (gate_up + SwiGLU)",
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": nbytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3)}
 
     cpu = None
