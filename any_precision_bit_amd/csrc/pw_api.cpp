@@ -98,7 +98,6 @@ struct pw_layer_s {
     pw::RouteParams rp{};
     pw::BucketParams bp{};
     pw::GemmParams gp_gu{}, gp_dn{};
-    int lds_gu = 0, lds_dn = 0;
     const uint16_t* res_x = nullptr;
     const float* res_y = nullptr;
     uint16_t* res_out = nullptr;
@@ -236,14 +235,15 @@ pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
         case 1:
         case 2: {
             pw::GemmParams gp = phase == 1 ? L->gp_gu : L->gp_dn;
-            const int lds = phase == 1 ? L->lds_gu : L->lds_dn;
             const int mode = phase - 1;
             gp.list = mode == 0 ? pw::LIST_GU_SMALL : pw::LIST_DN_SMALL;
-            if ((e = pw::launch_gemm(mode, 32, gp, lds, wg_small, s)) != hipSuccess)
+            if ((e = pw::launch_gemm(mode, pw::kSmallTokens, gp, pw::gemm_lds_bytes(pw::kSmallTokens), wg_small,
+                                     s)) != hipSuccess)
                 return hip_fail(e, mode == 0 ? "gate_up kernel" : "down kernel");
-            if (T > 32) {
+            if (T > pw::kSmallTokens) {
                 gp.list = mode == 0 ? pw::LIST_GU_LARGE : pw::LIST_DN_LARGE;
-                if ((e = pw::launch_gemm(mode, 128, gp, lds, wg_large, s)) != hipSuccess)
+                if ((e = pw::launch_gemm(mode, pw::kLargeTokens, gp, pw::gemm_lds_bytes(pw::kLargeTokens), wg_large,
+                                         s)) != hipSuccess)
                     return hip_fail(e, mode == 0 ? "gate_up kernel (large)" : "down kernel (large)");
             }
             break;
@@ -433,14 +433,12 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     gp.shared_base = D.max_tokens * k;
     gp.y = y;
     // gate_up + SwiGLU: items of 32 rows of F (gate and up)
-    L->lds_gu = pw::gemm_lds_bytes();
     L->gp_gu = gp;
     L->gp_gu.tiles_r = D.d_ffn / 32;
     L->gp_gu.tiles_s = D.d_ffn_shared / 32;
     L->gp_gu.pieces_r = L->gp_gu.pieces_s = 1;
     L->gp_gu.b_bytes = (uint32_t)((size_t)D.max_tokens * d * 2);
     // down + weighted scatter-accumulate: items of 64 rows of d
-    L->lds_dn = pw::gemm_lds_bytes();
     L->gp_dn = gp;
     L->gp_dn.tiles_r = d / 64;
     L->gp_dn.tiles_s = has_shared ? d / 64 : 0;

@@ -61,8 +61,9 @@ struct BucketParams {
 };
 
 // Dequantising GEMM over (expert, row tile, K-piece, token group) items of one
-// list. An item covers 32 rows of each of two row-sets; wave w of the
-// work-group owns the 256-column chunks w, w+4, ... of the item's K range.
+// list. An item covers 32 rows of each of two row-sets over its K range; wave w
+// of the work-group owns rows 16*(w >> 1) .. +15 and half-line w & 1 of every
+// 128-byte plane line.
 // gate_up: set 0 = gate rows [f0, f0+32), set 1 = up rows [f0, f0+32), K = d,
 //          B = xperm rows (tokens), epilogue SwiGLU -> act (fp16).
 // down:    set 0 = rows [r0, r0+32), set 1 = rows [r0+32, r0+64), K = F (in
@@ -86,7 +87,7 @@ struct GemmParams {
 hipError_t launch_init_ws(const Workspace& ws, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_bucket(const BucketParams& p, hipStream_t s);
-// tile_tokens: 32 (one MFMA token tile per item) or 128 (four tiles).
+// tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
 hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
                        hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
@@ -94,9 +95,11 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, 
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
-// LDS bytes of the gemm kernels.
-int gemm_lds_bytes();
+// LDS bytes of the gemm kernels for items of tile_tokens tokens.
+int gemm_lds_bytes(int tile_tokens);
 
+constexpr int kSmallTokens = 16;          // experts with 1..16 tokens: one 16-token MFMA tile
+constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
 constexpr int kRouteThreads = 512;
 constexpr int kBucketThreads = 1024;

@@ -40,7 +40,7 @@
 namespace pw {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const _Float16 lds_half;
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketParams p) 
         tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
         pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
     }
-    const int small = (cnt >= 1 && cnt <= 32) ? 1 : 0;
-    const int groups = cnt > 32 ? (cnt + 127) / 128 : 0;
+    const int small = (cnt >= 1 && cnt <= kSmallTokens) ? 1 : 0;
+    const int groups = cnt > kSmallTokens ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
     const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn, groups * p.tiles_dn * pdn};
     const int stride = E + 2;
     for (int l = 0; l < N_LISTS; ++l) {
@@ -592,14 +592,6 @@ __device__ __forceinline__ void lut_stage_load(LutStage& st, const uint16_t* lut
         }
     }
 }
-__device__ __forceinline__ void lut_stage_write(uint32_t* stripe, const LutStage& st, int bmax, int tid) {
-    const int total = lut_units(bmax);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int j = tid + it * 256;
-        if (j < total) write_stripe8(stripe, (j >> 5) * 8, j & 31, 1 << bmax, st.v0[it], st.v1[it]);
-    }
-}
 
 // Same layout for 32 rows of one LUT (both halves), one wave, plain loop.
 __device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* lut, int b, int lane) {
@@ -673,8 +665,8 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     const int piece = (local / tiles) % pieces;
     it.grp = local / tiles / pieces;
     it.n_tok = sh ? p.T : kconst(p.ws.counts)[it.ex];
-    it.tbase = it.grp * 32 * NT;
-    it.nl = min(32 * NT, it.n_tok - it.tbase);
+    it.tbase = it.grp * 16 * NT;
+    it.nl = min(16 * NT, it.n_tok - it.tbase);
     if (MODE == 0) {
         it.K = p.d;
         it.R = sh ? p.Fs : p.F;
@@ -693,39 +685,77 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     return it;
 }
 
-// LDS of the gemm kernels: a 64 KiB stripe whose 256-byte row idx holds, in
-// dwords 0..31, the LUT entry idx of the item's 32 row slots (low half: set 0,
-// high half: set 1) and, in dwords 32..63, the cross-wave reduction buffer;
-// then the token rows of two items (double buffer), the work-list prefix and
-// the item hand-over words.
+// LDS of the gemm kernels: a 64 KiB LUT stripe whose 256-byte row idx holds, in
+// dword 32*h + 16*c + r, the LUT entry idx of item row 16*h + r (low half: set
+// 0, high half: set 1), in two copies c so that the 32 lanes of a half-wave
+// (rows r, copies kg & 1) hit 32 distinct banks; then the cross-wave partial
+// sums, the token rows of two items (double buffer), the work-list prefix and
+// the item ring.
 constexpr int kStripeBytes = 65536;
-constexpr int kTokWords = 3 * 128;   // brow, orow, weight bits of up to 128 tokens
+constexpr int kTokWords = 3 * 64;   // brow, orow, weight bits of up to 64 tokens
+
+__device__ __forceinline__ int stripe_slot(int row) {   // copy 0 of item row 0..31
+    return ((row >> 4) << 5) + (row & 15);
+}
+
+// Writes 8 consecutive entries (idx = c8..c8+7) of one item row, both copies.
+__device__ __forceinline__ void write_stripe8x2(uint32_t* stripe, int c8, int row, int nidx, uint4 a, uint4 b) {
+    uint32_t* dst = stripe + c8 * 64 + stripe_slot(row);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (av[i] & 0xFFFFu) | (bv[i] << 16);
+        const uint32_t hi = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
+        if (nidx >= 8 || 2 * i < nidx) {
+            dst[(2 * i) * 64] = lo;
+            dst[(2 * i) * 64 + 16] = lo;
+        }
+        if (nidx >= 8 || 2 * i + 1 < nidx) {
+            dst[(2 * i + 1) * 64] = hi;
+            dst[(2 * i + 1) * 64 + 16] = hi;
+        }
+    }
+}
+__device__ __forceinline__ void lut_stage_write(uint32_t* stripe, const LutStage& st, int bmax, int tid) {
+    const int total = lut_units(bmax);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int j = tid + it * 256;
+        if (j < total) write_stripe8x2(stripe, (j >> 5) * 8, j & 31, 1 << bmax, st.v0[it], st.v1[it]);
+    }
+}
 
 // Persistent work-group of 4 waves over the items of one list. An item is 32
-// rows of each of two row-sets over the item's K range; wave q owns the
-// 256-column chunks q, q+4, q+8, ... Lane (r, g) of each wave reads 16 bytes of
-// row r per plane and chunk, so for every 128-byte line of a plane row the four
-// waves read its four 32-byte quarters together and the line is fetched from
-// HBM once. The four partial sums meet in LDS; wave q finishes accumulator
-// registers 4q..4q+3 (rows 8q..8q+7 of the 32x32 tile).
-// MODE 0: gate_up, MODE 1: down. NT: token tiles of 32.
+// rows of each of two row-sets over the item's K range, read as 128-byte lines
+// (1024 columns of a plane row): wave q owns rows 16*(q >> 1) .. +15 of the
+// item and half-line q & 1 of every line, and lane (r, kg) of it loads 16
+// bytes (128 columns) of row r. A load instruction so covers 16 rows x 64
+// contiguous bytes, and the two waves of a row half read the two halves of each
+// line together. MFMA 16x16x32: A = 16 weight rows x 32 columns, B = 32 columns
+// x 16 tokens. The two half-line partial sums meet in LDS; wave (h, 0)
+// finishes accumulator registers 0, 1 (rows 4*rg + 0, 1) and wave (h, 1)
+// registers 2, 3. The work-group keeps two items reserved, so the next item's
+// metadata is known while the current one runs: its first chunk and LUT rows
+// load during the current item's last chunk.
+// MODE 0: gate_up, MODE 1: down. NT: token tiles of 16.
 template <int MODE, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    // tid, r and g are re-declared opaque at every item (below) so that the
+    // tid, r, kg are re-declared opaque at every item (below) so that the
     // compiler recomputes values derived from them instead of keeping dozens of
     // them live across the persistent loop
     int tid = threadIdx.x;
     const int q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
-    int r = tid & 31, g = (tid >> 5) & 1;
+    const int rh = q >> 1, kh = q & 1;
+    int r = tid & 15, kg = (tid >> 4) & 3;
     uint32_t* stripe = (uint32_t*)smem;
-    int* s_tok = (int*)(smem + kStripeBytes);           // [2][kTokWords]
+    float* red = (float*)(smem + kStripeBytes);                  // [4 waves][NT][4][64]
+    int* s_tok = (int*)(red + 4 * NT * 4 * 64);                  // [2][kTokWords]
     int* s_pre = s_tok + 2 * kTokWords;
-    int* s_item = s_pre + PW_MAX_EXPERTS + 2;           // [0] first item, [1] reserved next item
+    int* s_ring = s_pre + PW_MAX_EXPERTS + 2;                    // reserved items
     const int npos = p.E + p.has_shared;
-    // Items are handed out by an atomic counter; each work-group holds one item in
-    // reserve so that its first chunks can be prefetched. The last work-group to
-    // leave resets the counters for the next launch.
+    // Items are handed out by an atomic counter, two ahead per work-group. The
+    // last work-group to leave resets the counters for the next launch.
     uint32_t* cnt = p.ws.sched + 2 * p.list;
     auto leave = [&]() {
         if (tid == 0 && atomicAdd(cnt + 1, 1u) == gridDim.x - 1) {
@@ -734,10 +764,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         }
     };
     for (int i = tid; i <= npos; i += 256) s_pre[i] = p.ws.prefix[p.list * (p.E + 2) + i];
-    if (tid == 0) s_item[0] = (int)atomicAdd(cnt, 1u);
+    if (tid == 0) {
+        s_ring[0] = (int)atomicAdd(cnt, 1u);
+        s_ring[1] = (int)atomicAdd(cnt, 1u);
+    }
     __syncthreads();
     const int n_items = __builtin_amdgcn_readfirstlane(s_pre[npos]);
-    int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    int item = __builtin_amdgcn_readfirstlane(s_ring[0]);
     if (item >= n_items) {
         leave();
         return;
@@ -747,24 +780,22 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
     const int ldb = MODE == 0 ? p.d : p.ld_act;
     const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(Bbase, p.b_bytes);
 
-    // reduction slot of (wave w, set s, accumulator register v) of this lane
-    auto red = [&](int w, int s, int v) -> float* {
-        return (float*)&stripe[((((w * 2 + s) * 16 + v) * 2 + g) << 6) + 32 + r];
-    };
-
     uint4 pa0[8], pa1[8], pb0[8], pb1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) pa0[i] = pa1[i] = pb0[i] = pb1[i] = make_uint4(0, 0, 0, 0);
 
-    // plane loads of chunk ch of an item into (c0, c1): slot i holds plane
-    // i - (8 - b); slots below 8 - b and lanes past the item's K range read zeros
+    // first column of this lane's 128 columns in chunk ch (relative to the item's K range)
+    auto lane_col = [&](int ch) { return ch * 1024 + kh * 512 + kg * 128; };
+    // plane loads of chunk ch (line ch of the item's K range) into (c0, c1):
+    // slot i holds plane i - (8 - b); absent planes and columns past the range read zeros
     auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
         const int Kb = it.K >> 3;
-        const bool vg = (ch * 256 + g * 128) < it.klen;
+        const bool vg = lane_col(ch) < it.klen;
         const uint32_t nrec = (uint32_t)(it.R * Kb);
-        const int cb = (it.kbase >> 3) + ch * 32 + g * 16;
-        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + r) * Kb + cb) : kOOB;
-        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + r) * Kb + cb) : kOOB;
+        const int cb = (it.kbase + lane_col(ch)) >> 3;
+        const int row = rh * 16 + r;
+        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + row) * Kb + cb) : kOOB;
+        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
         const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -772,20 +803,18 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
             c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
         }
     };
-    auto n_chunks = [](const Item& it) { return (it.klen + 255) >> 8; };
-    auto start_item = [&](const Item& it, LutStage& st, TokInfo& tk) {
-        if (q < n_chunks(it)) load_chunk(it, q, pa0, pa1);
+    auto n_chunks = [](const Item& it) { return (it.klen + 1023) >> 10; };
+    auto lut_load = [&](const Item& it, LutStage& st) {
         const int b0 = it.blk0->bits, b1 = it.blk1->bits;
         lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
                        (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
-        tk = fetch_tokinfo<MODE>(p, it, tid);
     };
     auto publish_item = [&](const Item& it, const LutStage& st, const TokInfo& tk, int par) {
         if (tid < it.nl) {
             int* tb = s_tok + par * kTokWords;
             tb[tid] = tk.brow;
-            tb[128 + tid] = tk.orow;
-            tb[256 + tid] = __float_as_int(tk.w);
+            tb[64 + tid] = tk.orow;
+            tb[128 + tid] = __float_as_int(tk.w);
         }
         const int b0 = it.blk0->bits, b1 = it.blk1->bits;
         lut_stage_write(stripe, st, b0 > b1 ? b0 : b1, tid);
@@ -794,56 +823,68 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
     Item it = decode_item<MODE, NT>(p, s_pre, npos, item);
     {
         LutStage st;
-        TokInfo tk;
-        start_item(it, st, tk);
+        const TokInfo tk = fetch_tokinfo<MODE>(p, it, tid);
+        load_chunk(it, 0, pa0, pa1);
+        lut_load(it, st);
         publish_item(it, st, tk, 0);
     }
     __syncthreads();
     int par = 0;
 
     while (true) {
-        asm volatile("" : "+v"(tid), "+v"(r), "+v"(g));
+        asm volatile("" : "+v"(tid), "+v"(r), "+v"(kg));
         const int nch = n_chunks(it);
-        const int ntl = (it.nl + 31) >> 5;
+        const int ntl = (it.nl + 15) >> 4;
         const int* tb = s_tok + par * kTokWords;
+        // the next item (reserved one item ago): its metadata and token rows now
+        const int next = __builtin_amdgcn_readfirstlane(s_ring[par ^ 1]);
+        const bool has_next = next < n_items;
+        Item nit = it;
+        TokInfo ntk{0, 0, 0.0f};
+        if (has_next) {
+            nit = decode_item<MODE, NT>(p, s_pre, npos, next);
+            ntk = fetch_tokinfo<MODE>(p, nit, tid);
+        }
 
         uint32_t boff[NT];
         bool bok[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int i = nt * 32 + r;
+            const int i = nt * 16 + r;
             bok[nt] = i < it.nl;
-            boff[nt] = bok[nt] ? (uint32_t)(tb[i] * ldb + g * 128) : 0u;
+            boff[nt] = bok[nt] ? (uint32_t)(tb[i] * ldb + kh * 512 + kg * 128) : 0u;
         }
-        floatx16 acc0[NT], acc1[NT];
+        floatx4 acc0[NT], acc1[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            acc0[nt] = (floatx16)0.0f;
-            acc1[nt] = (floatx16)0.0f;
+            acc0[nt] = (floatx4)0.0f;
+            acc1[nt] = (floatx4)0.0f;
         }
 
         auto load_b = [&](int ch, int dw, half8 (&bf)[NT][4], bool vg) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const uint32_t off =
-                    (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 256 + 32 * dw)) * 2u : kOOB;
+                    (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 1024 + 32 * dw)) * 2u : kOOB;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) bf[nt][m] = __builtin_bit_cast(half8, buf_load16(brsrc, off + 16u * m));
             }
         };
 
-        // One 256-column chunk: for each of the four 32-column dwords, transpose the
+        const uint32_t slot = lds_addr(smem) + (uint32_t)((rh * 32 + (kg & 1) * 16 + r) * 4);
+        // One chunk: for each of the lane's four 32-column dwords, transpose the
         // plane words of both sets, look the weights up and feed the MFMAs. The B
         // fragments of a dword (L2-resident activations) load at its start and
         // arrive while the transposes and lookups run. Lanes past K hold zero B
-        // fragments, so their A fragments need no masking.
-        const uint32_t slot = lds_addr(smem) + (uint32_t)(r * 4);
+        // fragments, so their A fragments need no masking. A wave whose half of
+        // the chunk lies wholly past K skips it.
         auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
-            const bool vg = (ch * 256 + g * 128) < it.klen;
-            half8 bfr[2][NT][4];
+            if (ch * 1024 + kh * 512 >= it.klen) return;
+            const bool vg = lane_col(ch) < it.klen;
+            half8 bfr[NT][4];
 #pragma unroll
             for (int dw = 0; dw < 4; ++dw) {
-                load_b(ch, dw, bfr[dw & 1], vg);
+                load_b(ch, dw, bfr, vg);
                 uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -859,95 +900,98 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
                         if (nt < ntl) {
-                            acc0[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bfr[dw & 1][nt][m], acc0[nt], 0, 0, 0);
-                            acc1[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bfr[dw & 1][nt][m], acc1[nt], 0, 0, 0);
+                            acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[nt][m], acc0[nt], 0, 0, 0);
+                            acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[nt][m], acc1[nt], 0, 0, 0);
                         }
                     }
                 }
             }
         };
 
-        // this wave's chunks q, q+4, ...: the first arrives in pa (prefetched with
-        // the item), later ones load into a buffer as soon as it has been
-        // consumed. Wave 0 reserves the next item when it starts on its last chunk.
-        int grab = 0;
-        if (q + 4 < nch) load_chunk(it, q + 4, pb0, pb1);
-#pragma unroll 1
-        for (int ch = q; ch < nch; ch += 8) {
-            if (tid == 0 && ch + 4 >= nch) grab = (int)atomicAdd(cnt, 1u);
-            compute_chunk(ch, pa0, pa1);
-            if (ch + 8 < nch) load_chunk(it, ch + 8, pa0, pa1);
-            if (ch + 4 >= nch) break;
-            if (tid == 0 && ch + 8 >= nch) grab = (int)atomicAdd(cnt, 1u);
-            compute_chunk(ch + 4, pb0, pb1);
-            if (ch + 12 < nch) load_chunk(it, ch + 12, pb0, pb1);
-        }
-
-        // partial sums of token tile nt for the other waves' accumulator registers
-        auto put_partials = [&](int nt) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                if ((v >> 2) != q) {
-                    *red(q, 0, v) = acc0[nt][v];
-                    *red(q, 1, v) = acc1[nt][v];
-                }
-            }
-        };
-        // sum of the four partials of registers 4q..4q+3 and the epilogue for them
-        auto finish = [&](int nt) {
-            const int tok_i = nt * 32 + r;
-            const bool tv = tok_i < it.nl;
-            const int orow = tv ? tb[128 + tok_i] : 0;
-            const float wv = tv ? __int_as_float(tb[256 + tok_i]) : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                if ((v >> 2) != q) continue;
-                float s0 = acc0[nt][v], s1 = acc1[nt][v];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    if (w != q) {
-                        s0 += *red(w, 0, v);
-                        s1 += *red(w, 1, v);
-                    }
-                }
-                if (!tv) continue;
-                const int row = q * 8 + g * 4 + (v & 3);
-                if (MODE == 0) {
-                    const float av = s0 / (1.0f + expf(-s0)) * s1;
-                    const int f = it.rows0 + row;
-                    p.ws.act[(size_t)orow * p.ld_act + (f & ~31) + perm32(f & 31)] = f2h(av);
-                } else {
-                    float* yr = p.y + (size_t)orow * p.d;
-                    unsafeAtomicAdd(yr + it.rows0 + row, wv * s0);
-                    unsafeAtomicAdd(yr + it.rows1 + row, wv * s1);
-                }
-            }
-        };
-
-        put_partials(0);
-        if (tid == 0) s_item[1] = grab;
-        __syncthreads();   // every wave is done with the LUT slots; partials and s_item[1] visible
-        const int next = __builtin_amdgcn_readfirstlane(s_item[1]);
-        const bool has_next = next < n_items;
-        Item nit = it;
+        // chunks 0, 1, ... alternate between (pa, pb); chunk 0 arrived with the
+        // item. The next item's first chunk and LUT rows load into pa / st as soon
+        // as pa has been consumed for the last time.
         LutStage st;
-        TokInfo ntk{0, 0, 0.0f};
-        if (has_next) {
-            nit = decode_item<MODE, NT>(p, s_pre, npos, next);
-            start_item(nit, st, ntk);
+        bool fetched = false;
+        auto fetch_next = [&]() {
+            if (has_next) {
+                load_chunk(nit, 0, pa0, pa1);
+                lut_load(nit, st);
+            }
+            fetched = true;
+        };
+        if (1 < nch) load_chunk(it, 1, pb0, pb1);
+#pragma unroll 1
+        for (int ch = 0; ch < nch; ch += 2) {
+            compute_chunk(ch, pa0, pa1);
+            if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
+            else if (ch + 1 < nch) fetch_next();
+            if (ch + 1 >= nch) break;
+            compute_chunk(ch + 1, pb0, pb1);
+            if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
         }
+        if (!fetched) fetch_next();
+
+        // partner (other half-line) partial sums of the registers it finishes
+        const int pq = q ^ 1;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt < ntl) {
+                float* w = red + ((q * NT + nt) * 4) * 64 + (tid & 63);
+                if (kh == 0) {
+                    w[0 * 64] = acc0[nt][2];
+                    w[1 * 64] = acc0[nt][3];
+                    w[2 * 64] = acc1[nt][2];
+                    w[3 * 64] = acc1[nt][3];
+                } else {
+                    w[0 * 64] = acc0[nt][0];
+                    w[1 * 64] = acc0[nt][1];
+                    w[2 * 64] = acc1[nt][0];
+                    w[3 * 64] = acc1[nt][1];
+                }
+            }
+        }
+        __syncthreads();   // every wave is done with the LUT stripe; partial sums visible
+        if (tid == 0) s_ring[par] = (int)atomicAdd(cnt, 1u);   // the item after next
+        if (has_next) publish_item(nit, st, ntk, par ^ 1);
+
+        // sum of the two half-line partials of registers 2*kh, 2*kh+1 and the epilogue
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt >= ntl) break;
-            if (nt > 0) {
-                __syncthreads();   // tile nt-1's partials have been read
-                put_partials(nt);
-                __syncthreads();
+            const int tok_i = nt * 16 + r;
+            const bool tv = tok_i < it.nl;
+            const float* pr = red + ((pq * NT + nt) * 4) * 64 + (tid & 63);
+            float g0, g1, u0, u1;
+            if (kh == 0) {
+                g0 = acc0[nt][0]; g1 = acc0[nt][1]; u0 = acc1[nt][0]; u1 = acc1[nt][1];
+            } else {
+                g0 = acc0[nt][2]; g1 = acc0[nt][3]; u0 = acc1[nt][2]; u1 = acc1[nt][3];
             }
-            finish(nt);
+            g0 += pr[0 * 64];
+            g1 += pr[1 * 64];
+            u0 += pr[2 * 64];
+            u1 += pr[3 * 64];
+            if (tv) {
+                const int row = rh * 16 + kg * 4 + kh * 2;   // rows row, row+1 of the item
+                const int orow = tb[64 + tok_i];
+                if (MODE == 0) {
+                    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
+                    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
+                    const int f = it.rows0 + row;   // even: f, f+1 are adjacent permuted columns
+                    const uint32_t pk = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
+                    *(uint32_t*)(p.ws.act + (size_t)orow * p.ld_act + (f & ~31) + perm32(f & 31)) = pk;
+                } else {
+                    const float wv = __int_as_float(tb[128 + tok_i]);
+                    float* yr = p.y + (size_t)orow * p.d;
+                    unsafeAtomicAdd(yr + it.rows0 + row, wv * g0);
+                    unsafeAtomicAdd(yr + it.rows0 + row + 1, wv * g1);
+                    unsafeAtomicAdd(yr + it.rows1 + row, wv * u0);
+                    unsafeAtomicAdd(yr + it.rows1 + row + 1, wv * u1);
+                }
+            }
         }
-        if (has_next) publish_item(nit, st, ntk, par ^ 1);
-        __syncthreads();   // next item's LUT slots and token rows are in place; partials read
+        __syncthreads();   // next item's LUT rows and token rows are in place; partials read
         if (!has_next) break;
         item = next;
         it = nit;
@@ -1033,8 +1077,9 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
 
 // ============================================================================ launchers
 
-int gemm_lds_bytes() {
-    return kStripeBytes + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4 + 2 * 4;
+int gemm_lds_bytes(int tile_tokens) {
+    const int nt = tile_tokens / 16;
+    return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4 + 2 * 4;
 }
 
 hipError_t launch_init_ws(const Workspace& ws, hipStream_t s) {
@@ -1068,11 +1113,11 @@ static hipError_t launch_gemm_t(const GemmParams& p, int lds_bytes, int n_wg, hi
 hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
                        hipStream_t s) {
     if (mode == 0) {
-        return tile_tokens == 32 ? launch_gemm_t<0, 1>(p, lds_bytes, n_wg, s)
-                                 : launch_gemm_t<0, 4>(p, lds_bytes, n_wg, s);
+        return tile_tokens == kSmallTokens ? launch_gemm_t<0, 1>(p, lds_bytes, n_wg, s)
+                                           : launch_gemm_t<0, 4>(p, lds_bytes, n_wg, s);
     }
-    return tile_tokens == 32 ? launch_gemm_t<1, 1>(p, lds_bytes, n_wg, s)
-                             : launch_gemm_t<1, 4>(p, lds_bytes, n_wg, s);
+    return tile_tokens == kSmallTokens ? launch_gemm_t<1, 1>(p, lds_bytes, n_wg, s)
+                                       : launch_gemm_t<1, 4>(p, lds_bytes, n_wg, s);
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
