@@ -44,6 +44,12 @@ class pw_route_out(ctypes.Structure):
 
 
 def _load():
+    # PyTorch supplies device memory and streams; its HIP runtime must be the one
+    # libpw.so binds to, so it is loaded first (one HIP runtime per process).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                           "or python any_precision_bit_amd/build.py")

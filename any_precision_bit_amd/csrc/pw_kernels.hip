@@ -569,37 +569,41 @@ __device__ __forceinline__ void write_stripe8(uint32_t* stripe, int c8, int row,
     }
 }
 
-// LUT entries of an item's 32 rows of both row-sets, eight per load: unit j
-// covers row j & 31, entries 8*(j >> 5) .. +7. At most 4 units per thread (b = 8).
-// The loads are issued early (lut_stage_load) and written to the stripe later
-// (lut_stage_write), so their latency hides behind other work.
+// LUT pages are stored in 32-row tiles: a tile holds, for entry group g =
+// 0 .. max(1, 2^b/8) - 1, the entries [8g, 8g + min(8, 2^b)) of its 32 rows, row
+// after row. The tile of an item's 32 rows of one row-set is 32 * 2^b contiguous
+// fp16 values, staged with coalesced 16-byte loads: thread t takes units t,
+// t + 256, ... (4 * 2^b units per set, at most 4 per thread at b = 8). For
+// b >= 3 unit u is entries 8*(u >> 5) .. +7 of row u & 31. The loads are issued
+// early (lut_stage_load) and written to the stripe later (lut_stage_write).
 struct LutStage {
-    uint4 v0[4], v1[4];
+    uint4 v[2][4];
 };
-__device__ __forceinline__ int lut_units(int bmax) {
-    return ((1 << bmax) >= 8 ? (1 << bmax) / 8 : 1) * 32;
-}
 __device__ __forceinline__ void lut_stage_load(LutStage& st, const uint16_t* lut0, int b0,
                                                const uint16_t* lut1, int b1, int tid) {
-    const int total = lut_units(b0 > b1 ? b0 : b1);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const int j = tid + it * 256;
-        if (j < total) {
-            const int r = j & 31, c8 = (j >> 5) * 8;
-            st.v0[it] = load_lut8(lut0 + ((size_t)r << b0), b0, c8);
-            st.v1[it] = load_lut8(lut1 + ((size_t)r << b1), b1, c8);
-        }
+        const int u = tid + it * 256;
+        st.v[0][it] = u < (4 << b0) ? *(const uint4*)(lut0 + 8 * u) : make_uint4(0, 0, 0, 0);
+        st.v[1][it] = u < (4 << b1) ? *(const uint4*)(lut1 + 8 * u) : make_uint4(0, 0, 0, 0);
     }
 }
 
-// Same layout for 32 rows of one LUT (both halves), one wave, plain loop.
-__device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* lut, int b, int lane) {
+// Debug-kernel stripe (dword idx*64 + row, both halves the same) from one
+// 32-row LUT tile, one wave, plain loop.
+__device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* tile, int b, int lane) {
     const int nidx = 1 << b;
-    const int total = (nidx >= 8 ? nidx / 8 : 1) * 32;
-    for (int j = lane; j < total; j += 64) {
-        const uint4 v = load_lut8(lut + ((size_t)(j & 31) << b), b, (j >> 5) * 8);
-        write_stripe8(stripe, (j >> 5) * 8, j & 31, nidx, v, v);
+    for (int e = lane; e < 32 * nidx; e += 64) {
+        int row, idx;
+        if (b >= 3) {
+            row = (e >> 3) & 31;
+            idx = ((e >> 8) << 3) | (e & 7);
+        } else {
+            row = e >> b;
+            idx = e & (nidx - 1);
+        }
+        const uint32_t h = tile[e];
+        stripe[idx * 64 + row] = h | (h << 16);
     }
 }
 
@@ -698,30 +702,60 @@ __device__ __forceinline__ int stripe_slot(int row) {   // copy 0 of item row 0.
     return ((row >> 4) << 5) + (row & 15);
 }
 
-// Writes 8 consecutive entries (idx = c8..c8+7) of one item row, both copies.
-__device__ __forceinline__ void write_stripe8x2(uint32_t* stripe, int c8, int row, int nidx, uint4 a, uint4 b) {
-    uint32_t* dst = stripe + c8 * 64 + stripe_slot(row);
-    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+// Writes the staged LUT units of both row-sets into the stripe: entry idx of
+// item row `row` of set s is the 16-bit half s of dword idx*64 + slot (copy 0)
+// and of dword idx*64 + slot + 16 (copy 1). When both sets have b >= 3, unit u
+// holds the same (entry group, row) of both, and one dword write stores both
+// halves (entries past the smaller set's 2^b are never read); each half-wave
+// writes rows 0..31 and the copy order alternates with the row half, so every
+// write instruction hits 32 distinct banks. Otherwise each set writes its own
+// halves.
+__device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const LutStage& st, int b0, int b1, int tid) {
+    if (b0 >= 3 && b1 >= 3) {
+        const int bmax = b0 > b1 ? b0 : b1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (av[i] & 0xFFFFu) | (bv[i] << 16);
-        const uint32_t hi = (av[i] >> 16) | (bv[i] & 0xFFFF0000u);
-        if (nidx >= 8 || 2 * i < nidx) {
-            dst[(2 * i) * 64] = lo;
-            dst[(2 * i) * 64 + 16] = lo;
+        for (int it = 0; it < 4; ++it) {
+            const int u = tid + it * 256;
+            if (u >= (4 << bmax)) continue;
+            const int row = u & 31, h = (row >> 4) & 1;
+            uint32_t* base = (uint32_t*)stripe + ((u >> 5) << 9) + stripe_slot(row);   // idx0 = 8 * (u >> 5)
+            const uint32_t a[4] = {st.v[0][it].x, st.v[0][it].y, st.v[0][it].z, st.v[0][it].w};
+            const uint32_t c[4] = {st.v[1][it].x, st.v[1][it].y, st.v[1][it].z, st.v[1][it].w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t lo = k & 1 ? (a[k >> 1] >> 16) : (a[k >> 1] & 0xFFFFu);
+                const uint32_t hi = k & 1 ? (c[k >> 1] & 0xFFFF0000u) : (c[k >> 1] << 16);
+                base[k * 64 + 16 * h] = lo | hi;
+                base[k * 64 + 16 * (1 - h)] = lo | hi;
+            }
         }
-        if (nidx >= 8 || 2 * i + 1 < nidx) {
-            dst[(2 * i + 1) * 64] = hi;
-            dst[(2 * i + 1) * 64 + 16] = hi;
-        }
+        return;
     }
-}
-__device__ __forceinline__ void lut_stage_write(uint32_t* stripe, const LutStage& st, int bmax, int tid) {
-    const int total = lut_units(bmax);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int j = tid + it * 256;
-        if (j < total) write_stripe8x2(stripe, (j >> 5) * 8, j & 31, 1 << bmax, st.v0[it], st.v1[it]);
+    for (int s = 0; s < 2; ++s) {
+        const int b = s ? b1 : b0;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int u = tid + it * 256;
+            if (u >= (4 << b)) continue;
+            const uint4 v = st.v[s][it];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                int row, idx;
+                if (b >= 3) {
+                    row = u & 31;
+                    idx = ((u >> 5) << 3) + k;
+                } else {
+                    row = (8 * u + k) >> b;
+                    idx = (8 * u + k) & ((1 << b) - 1);
+                }
+                const uint16_t hv = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+                unsigned char* at = stripe + (idx * 64 + stripe_slot(row)) * 4 + 2 * s;
+                *(uint16_t*)at = hv;
+                *(uint16_t*)(at + 64) = hv;
+            }
+        }
     }
 }
 
@@ -816,8 +850,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
             tb[64 + tid] = tk.orow;
             tb[128 + tid] = __float_as_int(tk.w);
         }
-        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
-        lut_stage_write(stripe, st, b0 > b1 ? b0 : b1, tid);
+        lut_stage_write(smem, st, it.blk0->bits, it.blk1->bits, tid);
     };
 
     Item it = decode_item<MODE, NT>(p, s_pre, npos, item);

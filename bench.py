@@ -75,6 +75,7 @@ def main():
 
     import synth
     from any_precision_bit_amd import PagedMoELayer
+    from any_precision_bit_amd.pages import lut_page
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -105,7 +106,7 @@ def main():
     for (e, lin), blk in blocks.items():
         b = int(bits[e, lin])
         base_pages[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes[:b])).to(dev),
-                                f16(blk.luts[b]), b)
+                                f16(lut_page(blk.luts[b])), b)
     x = f16(x_h)
     clones = []
     for c in range(args.clones):

@@ -30,7 +30,10 @@
  *     bit of q) is R * K/8 bytes, row-major with row stride K/8 bytes; column c
  *     of a row is bit (c & 7) of byte (c >> 3).
  *   - at bitwidth b the weight is LUT_b[r][q >> (8-b)], read from planes 0..b-1;
- *     LUT_b is R * 2^b fp16 values, row-major (one table per output row).
+ *     LUT_b has one table of 2^b fp16 entries per output row r (R * 2^b values),
+ *     stored in 32-row tiles: with E = min(8, 2^b) and G = 2^b / E, entry i of
+ *     row r sits at element ((t*G + g)*32 + rr)*E + j, where t = r / 32,
+ *     rr = r % 32, g = i / E, j = i % E (R must be a multiple of 32).
  */
 #ifndef PW_H
 #define PW_H
@@ -114,8 +117,8 @@ pw_status pw_moe_plan_set(pw_layer layer, const uint8_t* bits, int32_t n_blocks)
 /* Binds the pages of block (expert, linear): planes[p] for p < n_planes are
  * device pointers to bit-plane p (planes 0..n_planes-1 of the parent, 16-byte
  * aligned, R*K/8 bytes each); lut is a device pointer to LUT_{lut_bits}
- * (R * 2^lut_bits fp16, 16-byte aligned). The host array `planes` is copied
- * before return. The pages must stay alive until every forward enqueued while
+ * (R * 2^lut_bits fp16 in the tiled order above, 16-byte aligned). The host
+ * array `planes` is copied before return. The pages must stay alive until every forward enqueued while
  * they were bound has completed on its stream. A forward requires, for every
  * block, n_planes >= b and lut_bits == b for the planned b (else PW_E_UNBOUND). */
 pw_status pw_page_table_bind(pw_layer layer, int32_t expert, int32_t linear,
@@ -161,7 +164,8 @@ pw_status pw_layer_last_bytes(pw_layer layer, void* stream, double* bytes /*[4]*
 
 /* Test hooks for one block, same kernels' dequantisation path as the forward:
  * indices u8 [R][K] of bitwidth b (pw_debug_unpack) and weights fp16 [R][K]
- * (pw_debug_dequant), for an [R x K] block with R % 32 == 0 and K % 128 == 0.
+ * (pw_debug_dequant, lut in the tiled order above), for an [R x K] block with
+ * R % 32 == 0 and K % 128 == 0.
  * All pointers are device pointers; the call is asynchronous on `stream`. */
 pw_status pw_debug_unpack(const void* const* planes, int32_t b, int32_t R, int32_t K,
                           uint8_t* idx_out, void* stream);

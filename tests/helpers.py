@@ -20,8 +20,9 @@ def rel_err_per_token(y, ref):
 
 def device_pages(blocks, bits, device, all_luts=False):
     """Copies each block's planes 0..b-1 (all generated planes when all_luts)
-    and its LUT(s) to the device. Returns {(e, lin): (planes u8 [n,R,K/8], {b: lut fp16})}."""
+    and its LUT(s), in the tiled LUT page order, to the device. Returns {(e, lin): (planes u8 [n,R,K/8], {b: lut fp16})}."""
     import torch
+    from any_precision_bit_amd.pages import lut_page
 
     out = {}
     for (e, lin), blk in blocks.items():
@@ -29,8 +30,8 @@ def device_pages(blocks, bits, device, all_luts=False):
         n = blk.planes.shape[0] if all_luts else b
         planes = torch.from_numpy(np.ascontiguousarray(blk.planes[:n])).to(device)
         lb = blk.luts.keys() if all_luts else [b]
-        luts = {int(bb): torch.from_numpy(blk.luts[bb].view(np.int16).copy()).to(device).view(torch.float16)
-                for bb in lb}
+        luts = {int(bb): torch.from_numpy(lut_page(blk.luts[bb]).view(np.int16).copy()).to(device)
+                .view(torch.float16) for bb in lb}
         out[(e, lin)] = (planes, luts)
     return out
 

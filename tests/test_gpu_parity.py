@@ -29,6 +29,7 @@ def _say(*a):
 def test_unpack_and_dequant_bit_exact(torch_dev, R, K):
     torch, dev = torch_dev
     from any_precision_bit_amd import binding as B
+    from any_precision_bit_amd.pages import lut_page
 
     rng = np.random.default_rng(R + K)
     q = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
@@ -42,7 +43,7 @@ def test_unpack_and_dequant_bit_exact(torch_dev, R, K):
         ref_idx = oracle.unpack_indices(planes_h, b)
         assert np.array_equal(idx.cpu().numpy(), ref_idx), b
         lut_h = (rng.standard_normal((R, 1 << b)) * 0.02).astype(np.float16)
-        lut = to_dev_f16(lut_h, dev)
+        lut = to_dev_f16(lut_page(lut_h), dev)
         w = torch.zeros((R, K), dtype=torch.float16, device=dev)
         B.pw_debug_dequant([planes[p].data_ptr() for p in range(b)], b, lut.data_ptr(), R, K, w.data_ptr())
         torch.cuda.synchronize()
