@@ -150,7 +150,6 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
     const size_t o_st = off;     off += al(sizeof(uint32_t));
-    const size_t o_sc = off;     off += al(sizeof(uint32_t) * 2 * pw::N_LISTS);
     hipError_t e;
     int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess)
@@ -178,7 +177,6 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
-    L->ws.sched = (uint32_t*)(b + o_sc);
     for (int i = 0; i < kStageSlots; ++i) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
             hipSuccess) {

@@ -36,7 +36,6 @@ struct Workspace {
     uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
-    uint32_t* sched;     // [N_LISTS][2] work-item counter and exit counter per gemm list
 };
 
 struct RouteParams {

@@ -693,8 +693,7 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
 // dword 32*h + 16*c + r, the LUT entry idx of item row 16*h + r (low half: set
 // 0, high half: set 1), in two copies c so that the 32 lanes of a half-wave
 // (rows r, copies kg & 1) hit 32 distinct banks; then the cross-wave partial
-// sums, the token rows of two items (double buffer), the work-list prefix and
-// the item ring.
+// sums, the token rows of two items (double buffer) and the work-list prefix.
 constexpr int kStripeBytes = 65536;
 constexpr int kTokWords = 3 * 64;   // brow, orow, weight bits of up to 64 tokens
 
@@ -768,9 +767,9 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 // line together. MFMA 16x16x32: A = 16 weight rows x 32 columns, B = 32 columns
 // x 16 tokens. The two half-line partial sums meet in LDS; wave (h, 0)
 // finishes accumulator registers 0, 1 (rows 4*rg + 0, 1) and wave (h, 1)
-// registers 2, 3. The work-group keeps two items reserved, so the next item's
-// metadata is known while the current one runs: its first chunk and LUT rows
-// load during the current item's last chunk.
+// registers 2, 3. Items are assigned round-robin, so the next item's metadata
+// is known while the current one runs: its first chunk and LUT rows load
+// during the current item's last chunk.
 // MODE 0: gate_up, MODE 1: down. NT: token tiles of 16.
 template <int MODE, int NT>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p) {
@@ -786,29 +785,14 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
     float* red = (float*)(smem + kStripeBytes);                  // [4 waves][NT][4][64]
     int* s_tok = (int*)(red + 4 * NT * 4 * 64);                  // [2][kTokWords]
     int* s_pre = s_tok + 2 * kTokWords;
-    int* s_ring = s_pre + PW_MAX_EXPERTS + 2;                    // reserved items
     const int npos = p.E + p.has_shared;
-    // Items are handed out by an atomic counter, two ahead per work-group. The
-    // last work-group to leave resets the counters for the next launch.
-    uint32_t* cnt = p.ws.sched + 2 * p.list;
-    auto leave = [&]() {
-        if (tid == 0 && atomicAdd(cnt + 1, 1u) == gridDim.x - 1) {
-            atomicExch(cnt, 0u);
-            atomicExch(cnt + 1, 0u);
-        }
-    };
+    // Work-group w takes items w, w + G, w + 2G, ... of the list (G = grid size):
+    // no shared counter, and the next item is always known in advance.
     for (int i = tid; i <= npos; i += 256) s_pre[i] = p.ws.prefix[p.list * (p.E + 2) + i];
-    if (tid == 0) {
-        s_ring[0] = (int)atomicAdd(cnt, 1u);
-        s_ring[1] = (int)atomicAdd(cnt, 1u);
-    }
     __syncthreads();
     const int n_items = __builtin_amdgcn_readfirstlane(s_pre[npos]);
-    int item = __builtin_amdgcn_readfirstlane(s_ring[0]);
-    if (item >= n_items) {
-        leave();
-        return;
-    }
+    int item = blockIdx.x;
+    if (item >= n_items) return;
 
     const uint16_t* Bbase = MODE == 0 ? p.ws.xperm : p.ws.act;
     const int ldb = MODE == 0 ? p.d : p.ld_act;
@@ -869,8 +853,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         const int nch = n_chunks(it);
         const int ntl = (it.nl + 15) >> 4;
         const int* tb = s_tok + par * kTokWords;
-        // the next item (reserved one item ago): its metadata and token rows now
-        const int next = __builtin_amdgcn_readfirstlane(s_ring[par ^ 1]);
+        // the next item: its metadata and token rows now
+        const int next = item + (int)gridDim.x;
         const bool has_next = next < n_items;
         Item nit = it;
         TokInfo ntk{0, 0, 0.0f};
@@ -985,7 +969,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
             }
         }
         __syncthreads();   // every wave is done with the LUT stripe; partial sums visible
-        if (tid == 0) s_ring[par] = (int)atomicAdd(cnt, 1u);   // the item after next
         if (has_next) publish_item(nit, st, ntk, par ^ 1);
 
         // sum of the two half-line partials of registers 2*kh, 2*kh+1 and the epilogue
@@ -1030,7 +1013,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
         it = nit;
         par ^= 1;
     }
-    leave();
 }
 
 // ============================================================================ residual / init / debug
@@ -1043,7 +1025,6 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
 
 __global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws) {
     if (threadIdx.x == 0) *ws.status = 0u;
-    if (threadIdx.x < 2 * N_LISTS) ws.sched[threadIdx.x] = 0u;
 }
 
 struct DebugParams {
@@ -1112,7 +1093,7 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
 
 int gemm_lds_bytes(int tile_tokens) {
     const int nt = tile_tokens / 16;
-    return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4 + 2 * 4;
+    return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4;
 }
 
 hipError_t launch_init_ws(const Workspace& ws, hipStream_t s) {
