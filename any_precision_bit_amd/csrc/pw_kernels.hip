@@ -109,26 +109,18 @@ __device__ __forceinline__ void add_pair(uint32_t xw, uint32_t ww, long long& ac
     }
 }
 
-__device__ __forceinline__ void fma_pair(uint32_t xw, uint32_t ww, float& acc, float& sab) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float xf = h2f((uint16_t)(xw >> (16 * h)));
-        const float wf = h2f((uint16_t)(ww >> (16 * h)));
-        acc = fmaf(xf, wf, acc);                 // the product of two fp16 values is exact in fp32
-        sab = fmaf(fabsf(xf), fabsf(wf), sab);
-    }
-}
-
 // Key order of the top-k: larger value first, ties to the lower expert index.
 template <typename V>
 __device__ __forceinline__ bool key_gt(V va, int ea, V vb, int eb) {
     return va > vb || (va == vb && ea < eb);
 }
 
-// fp32 logit and bound of every expert e = wave + NW*i of one token. A row is NB
-// blocks of 512 columns (8 per lane); 32/NB rows are in flight per wave.
+// fp32 logit and bound of every expert e = wave + NW*j of one token. Columns
+// come in blocks of 512 (8 per lane); a wave issues the weight rows of BATCH
+// experts together, then reads each block of x (fp32, in LDS) once and applies
+// it to all of them.
 template <int NB>
-__device__ __forceinline__ void approx_logits(const RouteParams& p, const uint16_t* s_x, float* s_apx,
+__device__ __forceinline__ void approx_logits(const RouteParams& p, const float* s_xf, float* s_apx,
                                               float* s_bnd, int wave, int lane) {
     constexpr int NW = kRouteThreads / 64;
     constexpr int BATCH = NB >= 32 ? 1 : 32 / NB;
@@ -144,31 +136,44 @@ __device__ __forceinline__ void approx_logits(const RouteParams& p, const uint16
                 w[j][i] = (e < E && c < d) ? *(const uint4*)(p.wr + (size_t)e * d + c) : make_uint4(0, 0, 0, 0);
             }
         }
+        float acc[BATCH], sab[BATCH];
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            const int e = e0 + NW * j;
-            if (e >= E) break;
-            float acc = 0.0f, sab = 0.0f;
+        for (int j = 0; j < BATCH; ++j) acc[j] = sab[j] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int c = lane * 8 + 512 * i;
-                if (c < d) {
-                    const uint4 xv = *(const uint4*)(s_x + c);
-                    fma_pair(xv.x, w[j][i].x, acc, sab);
-                    fma_pair(xv.y, w[j][i].y, acc, sab);
-                    fma_pair(xv.z, w[j][i].z, acc, sab);
-                    fma_pair(xv.w, w[j][i].w, acc, sab);
+        for (int i = 0; i < NB; ++i) {
+            const int c = lane * 8 + 512 * i;
+            if (c >= d) break;
+            const float4 xa = *(const float4*)(s_xf + c), xb = *(const float4*)(s_xf + c + 4);
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const uint32_t wv[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    // the product of two fp16 values is exact in fp32
+                    const float wf = h2f((uint16_t)(wv[h >> 1] >> (16 * (h & 1))));
+                    acc[j] = fmaf(xv[h], wf, acc[j]);
+                    sab[j] = fmaf(fabsf(xv[h]), fabsf(wf), sab[j]);
                 }
             }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) {
-                acc += __shfl_xor(acc, off);
-                sab += __shfl_xor(sab, off);
+                acc[j] += __shfl_xor(acc[j], off);
+                sab[j] += __shfl_xor(sab[j], off);
             }
-            if (lane == 0) {
-                const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
-                s_apx[e] = acc + bf;
-                s_bnd[e] = sab + fabsf(bf);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                const int e = e0 + NW * j;
+                if (e < E) {
+                    const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
+                    s_apx[e] = acc[j] + bf;
+                    s_bnd[e] = sab[j] + fabsf(bf);
+                }
             }
         }
     }
@@ -185,85 +190,59 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
     __shared__ __align__(16) uint16_t s_x[kMaxModel];
+    __shared__ __align__(16) float s_xf[kMaxModel];
     __shared__ float s_apx[PW_MAX_EXPERTS];
     __shared__ float s_bnd[PW_MAX_EXPERTS];
     __shared__ int s_cand[PW_MAX_EXPERTS];
     __shared__ long long s_ex[PW_MAX_EXPERTS];
+    __shared__ long long s_selv[PW_MAX_TOP_K];
+    __shared__ int s_sele[PW_MAX_TOP_K];
+    __shared__ float s_tau;
     __shared__ int s_ncand;
 
     const uint16_t* xr = p.x + (size_t)t * d;
-    for (int c = tid * 8; c < d; c += kRouteThreads * 8) *(uint4*)(s_x + c) = *(const uint4*)(xr + c);
+    for (int c = tid * 8; c < d; c += kRouteThreads * 8) {
+        const uint4 v = *(const uint4*)(xr + c);
+        *(uint4*)(s_x + c) = v;
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) s_xf[c + h] = h2f((uint16_t)(vv[h >> 1] >> (16 * (h & 1))));
+    }
     for (int c = tid; c < d; c += kRouteThreads) {
         p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
         p.y[(size_t)t * d + c] = 0.0f;
     }
+    if (tid == 0) s_ncand = 0;
     __syncthreads();
 
-    // ---- fp32 logits and their error bound, one wave per expert; a wave issues
-    // the weight rows of a batch of its experts before reducing any of them
+    // ---- fp32 logits and their error bound, one wave per expert
     switch ((d + 511) >> 9) {
-        case 1: approx_logits<1>(p, s_x, s_apx, s_bnd, wave, lane); break;
-        case 2: approx_logits<2>(p, s_x, s_apx, s_bnd, wave, lane); break;
-        case 3: case 4: approx_logits<4>(p, s_x, s_apx, s_bnd, wave, lane); break;
-        case 5: case 6: case 7: case 8: approx_logits<8>(p, s_x, s_apx, s_bnd, wave, lane); break;
-        default: approx_logits<16>(p, s_x, s_apx, s_bnd, wave, lane); break;
+        case 1: approx_logits<1>(p, s_xf, s_apx, s_bnd, wave, lane); break;
+        case 2: approx_logits<2>(p, s_xf, s_apx, s_bnd, wave, lane); break;
+        case 3: case 4: approx_logits<4>(p, s_xf, s_apx, s_bnd, wave, lane); break;
+        case 5: case 6: case 7: case 8: approx_logits<8>(p, s_xf, s_apx, s_bnd, wave, lane); break;
+        default: approx_logits<16>(p, s_xf, s_apx, s_bnd, wave, lane); break;
     }
     __syncthreads();
 
-    // ---- candidates: A_e >= a_k - 2*delta
-    if (wave == 0) {
-        float v[PW_MAX_EXPERTS / 64];
-        bool taken[PW_MAX_EXPERTS / 64];
+    // ---- candidates: A_e >= a_k - 2*delta. Thread e ranks expert e among all
+    // (number of experts ahead of it in key order); rank k-1 holds a_k.
+    if (tid < E) {
+        const float ve = s_apx[tid];
+        int rank = 0;
         float bm = 0.0f;
-#pragma unroll
-        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-            const int e = lane + 64 * q;
-            v[q] = e < E ? s_apx[e] : -INFINITY;
-            taken[q] = e >= E;
-            if (e < E) bm = fmaxf(bm, s_bnd[e]);
+        for (int e2 = 0; e2 < E; ++e2) {
+            rank += key_gt(s_apx[e2], e2, ve, tid) ? 1 : 0;
+            bm = fmaxf(bm, s_bnd[e2]);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-        float ak = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            float bv = -INFINITY;
-            int be = 0x7fffffff;
-#pragma unroll
-            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-                const int e = lane + 64 * q;
-                if (!taken[q] && key_gt(v[q], e, bv, be)) {
-                    bv = v[q];
-                    be = e;
-                }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (key_gt(ov, oe, bv, be)) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            ak = bv;
-#pragma unroll
-            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q)
-                if (be == lane + 64 * q) taken[q] = true;
+        if (rank == k - 1) {
+            // |A_e - L_e| <= gamma_(d+1) * sum|x w| + |bias|-rounding: (d+2) * 2^-24 covers both
+            const float delta = bm * (float)(d + 2) * 5.9604645e-8f * 1.001f + 1e-30f;
+            s_tau = ve - 2.0f * delta - fabsf(ve) * 2.4e-7f - 2.0f * delta * 2.4e-7f;
         }
-        // |A_e - L_e| <= gamma_(d+1) * sum|x w| + |bias|-rounding: (d+2) * 2^-24 covers both
-        const float delta = bm * (float)(d + 2) * 5.9604645e-8f * 1.001f + 1e-30f;
-        const float tau = ak - 2.0f * delta - fabsf(ak) * 2.4e-7f - 2.0f * delta * 2.4e-7f;
-        int base = 0;
-#pragma unroll
-        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-            const int e = lane + 64 * q;
-            const bool c = e < E && v[q] >= tau;
-            const unsigned long long m = __ballot(c);
-            if (c) s_cand[base + __popcll(m & __lanemask_lt())] = e;
-            base += __popcll(m);
-        }
-        if (lane == 0) s_ncand = base;
     }
+    __syncthreads();
+    if (tid < E && s_apx[tid] >= s_tau) s_cand[atomicAdd(&s_ncand, 1)] = tid;
     __syncthreads();
 
     // ---- exact logits of the candidates, one wave per candidate
@@ -302,56 +281,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     }
     __syncthreads();
 
-    // ---- exact top-k over the candidates, softmax over the selected logits
-    if (wave == 0) {
-        long long selv[PW_MAX_TOP_K];
-        int sele[PW_MAX_TOP_K];
-        bool taken[PW_MAX_EXPERTS / 64];
-#pragma unroll
-        for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) taken[q] = (lane + 64 * q) >= nc;
-        for (int j = 0; j < k; ++j) {
-            long long bv = LLONG_MIN;
-            int be = 0x7fffffff;
-#pragma unroll
-            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-                const int ci = lane + 64 * q;
-                if (!taken[q] && key_gt(s_ex[ci], s_cand[ci], bv, be)) {
-                    bv = s_ex[ci];
-                    be = s_cand[ci];
-                }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const long long ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (key_gt(ov, oe, bv, be)) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            selv[j] = bv;
-            sele[j] = be;
-#pragma unroll
-            for (int q = 0; q < PW_MAX_EXPERTS / 64; ++q) {
-                const int ci = lane + 64 * q;
-                if (ci < nc && s_cand[ci] == be) taken[q] = true;
-            }
+    // ---- exact top-k: rank of each candidate among the candidates
+    if (tid < nc) {
+        const long long v = s_ex[tid];
+        const int e = s_cand[tid];
+        int rank = 0;
+        for (int c2 = 0; c2 < nc; ++c2) rank += key_gt(s_ex[c2], s_cand[c2], v, e) ? 1 : 0;
+        if (rank < k) {
+            s_selv[rank] = v;
+            s_sele[rank] = e;
         }
-        if (lane == 0) {
-            float l[PW_MAX_TOP_K], ex[PW_MAX_TOP_K];
-            float s = 0.0f;
-            for (int j = 0; j < k; ++j) l[j] = ldexpf((float)selv[j], -48);
-            for (int j = 0; j < k; ++j) {
-                ex[j] = expf(l[j] - l[0]);
-                s += ex[j];
-            }
-            for (int j = 0; j < k; ++j) {
-                const float wj = ex[j] / s;
-                p.ws.ids[(size_t)t * k + j] = sele[j];
-                p.ws.w[(size_t)t * k + j] = wj;
-                if (p.o_ids) p.o_ids[(size_t)t * k + j] = sele[j];
-                if (p.o_w) p.o_w[(size_t)t * k + j] = wj;
-            }
+    }
+    __syncthreads();
+    // softmax over the selected logits (descending order)
+    if (tid == 0) {
+        float l[PW_MAX_TOP_K], ex[PW_MAX_TOP_K];
+        float s = 0.0f;
+        for (int j = 0; j < k; ++j) l[j] = ldexpf((float)s_selv[j], -48);
+        for (int j = 0; j < k; ++j) {
+            ex[j] = expf(l[j] - l[0]);
+            s += ex[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            const float wj = ex[j] / s;
+            p.ws.ids[(size_t)t * k + j] = s_sele[j];
+            p.ws.w[(size_t)t * k + j] = wj;
+            if (p.o_ids) p.o_ids[(size_t)t * k + j] = s_sele[j];
+            if (p.o_w) p.o_w[(size_t)t * k + j] = wj;
         }
     }
 }
