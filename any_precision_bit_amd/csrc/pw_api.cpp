@@ -150,6 +150,9 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
     const size_t o_st = off;     off += al(sizeof(uint32_t));
+    const int dep_stride = (L->f_max + pw::kDownPiece - 1) / pw::kDownPiece;
+    const int n_dep = (E + 1) * dep_stride + 1;
+    const size_t o_dep = off;    off += al(sizeof(uint32_t) * (size_t)n_dep);
     hipError_t e;
     int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess)
@@ -177,6 +180,8 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
+    L->ws.dep = (uint32_t*)(b + o_dep);
+    L->ws.dep_stride = dep_stride;
     for (int i = 0; i < kStageSlots; ++i) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
             hipSuccess) {
@@ -186,7 +191,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess)
             return hip_fail(e, "hipEventCreate");
     }
-    if ((e = pw::launch_init_ws(L->ws, s)) != hipSuccess) return hip_fail(e, "init workspace");
+    if ((e = pw::launch_init_ws(L->ws, n_dep, s)) != hipSuccess) return hip_fail(e, "init workspace");
     L->dev_ready = true;
     return PW_OK;
 }
@@ -219,41 +224,38 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
 
 
 // Enqueues the kernels of one phase of the forward recorded in L:
-// 0 routing (router + bucket sort), 1 gate_up + SwiGLU, 2 down + accumulation,
-// 3 residual hand-off.
+// 0 routing (router + bucket sort), 1 experts (gate_up + SwiGLU + down +
+// accumulation), 2 residual hand-off.
 pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
     const int T = L->last_T;
-    const int wg_small = 2 * L->n_cu, wg_large = L->n_cu;   // resident work-groups per launch
     hipError_t e = hipSuccess;
     switch (phase) {
         case 0:
             if ((e = pw::launch_route(L->rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
             if ((e = pw::launch_bucket(L->bp, s)) != hipSuccess) return hip_fail(e, "bucket kernel");
             break;
-        case 1:
-        case 2: {
-            pw::GemmParams gp = phase == 1 ? L->gp_gu : L->gp_dn;
-            const int mode = phase - 1;
-            gp.list = mode == 0 ? pw::LIST_GU_SMALL : pw::LIST_DN_SMALL;
-            if ((e = pw::launch_gemm(mode, pw::kSmallTokens, gp, pw::gemm_lds_bytes(pw::kSmallTokens), wg_small,
-                                     s)) != hipSuccess)
-                return hip_fail(e, mode == 0 ? "gate_up kernel" : "down kernel");
+        case 1: {
+            pw::ExpertParams ep{L->gp_gu, L->gp_dn};
+            ep.gu.list = pw::LIST_GU_SMALL;
+            ep.dn.list = pw::LIST_DN_SMALL;
+            if ((e = pw::launch_experts(pw::kSmallTokens, ep, L->n_cu, s)) != hipSuccess)
+                return hip_fail(e, "expert kernel");
             if (T > pw::kSmallTokens) {
-                gp.list = mode == 0 ? pw::LIST_GU_LARGE : pw::LIST_DN_LARGE;
-                if ((e = pw::launch_gemm(mode, pw::kLargeTokens, gp, pw::gemm_lds_bytes(pw::kLargeTokens), wg_large,
-                                         s)) != hipSuccess)
-                    return hip_fail(e, mode == 0 ? "gate_up kernel (large)" : "down kernel (large)");
+                ep.gu.list = pw::LIST_GU_LARGE;
+                ep.dn.list = pw::LIST_DN_LARGE;
+                if ((e = pw::launch_experts(pw::kLargeTokens, ep, L->n_cu, s)) != hipSuccess)
+                    return hip_fail(e, "expert kernel (large)");
             }
             break;
         }
-        case 3:
+        case 2:
             if (L->res_out &&
                 (e = pw::launch_residual(L->res_x, L->res_y, L->res_out, (long)T * L->desc.d_model, s)) !=
                     hipSuccess)
                 return hip_fail(e, "residual kernel");
             break;
         default:
-            return fail(PW_E_ARG, "phase %d not in 0..3", phase);
+            return fail(PW_E_ARG, "phase %d not in 0..2", phase);
     }
     return PW_OK;
 }
@@ -447,7 +449,7 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     L->res_y = y;
     L->res_out = (uint16_t*)x_next;
 
-    for (int phase = 0; phase < 4; ++phase)
+    for (int phase = 0; phase < 3; ++phase)
         if ((st = launch_phase(L, phase, s)) != PW_OK) return st;
     if (getenv("PW_DEBUG_SYNC")) {
         hipError_t e = hipStreamSynchronize(s);
@@ -460,7 +462,7 @@ pw_status pw_moe_replay(pw_layer L, int32_t phase, void* stream) {
     g_err.clear();
     if (!L) return fail(PW_E_ARG, "pw_moe_replay: null layer");
     if (!L->dev_ready || L->last_T == 0) return fail(PW_E_STATE, "pw_moe_replay: no forward has run");
-    if (phase < 0 || phase > 3) return fail(PW_E_ARG, "phase %d not in 0..3", phase);
+    if (phase < 0 || phase > 2) return fail(PW_E_ARG, "phase %d not in 0..2", phase);
     DeviceGuard guard(L->device);
     if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
     return launch_phase(L, phase, (hipStream_t)stream);

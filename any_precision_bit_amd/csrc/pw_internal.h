@@ -36,6 +36,9 @@ struct Workspace {
     uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
+    uint32_t* dep;       // [(E+1)*dep_stride + 1]  gate_up items done per (list position, down
+                         //              K-piece); last word: work-groups finished (expert kernel)
+    int dep_stride;      // down K-pieces of the widest expert
 };
 
 struct RouteParams {
@@ -60,7 +63,7 @@ struct BucketParams {
 };
 
 // Dequantising GEMM over (expert, row tile, K-piece, token group) items of one
-// list. An item covers 32 rows of each of two row-sets over its K range; wave w
+// list (the expert kernel runs a gate_up list, then a down list). An item covers 32 rows of each of two row-sets over its K range; wave w
 // of the work-group owns rows 16*(w >> 1) .. +15 and half-line w & 1 of every
 // 128-byte plane line.
 // gate_up: set 0 = gate rows [f0, f0+32), set 1 = up rows [f0, f0+32), K = d,
@@ -83,19 +86,27 @@ struct GemmParams {
     float* y;
 };
 
-hipError_t launch_init_ws(const Workspace& ws, hipStream_t s);
+// One launch of the expert kernel: a gate_up list and the down list of the same
+// token-tile size (gu.list, dn.list); down items wait on gate_up items of their
+// expert through ws.dep.
+struct ExpertParams {
+    GemmParams gu;
+    GemmParams dn;
+};
+
+hipError_t launch_init_ws(const Workspace& ws, int n_dep, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_bucket(const BucketParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
-hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
-                       hipStream_t s);
+// The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).
+hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
                            hipStream_t s);
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
-// LDS bytes of the gemm kernels for items of tile_tokens tokens.
-int gemm_lds_bytes(int tile_tokens);
+// LDS bytes of the expert kernel for items of tile_tokens tokens.
+int expert_lds_bytes(int tile_tokens);
 
 constexpr int kSmallTokens = 16;          // experts with 1..16 tokens: one 16-token MFMA tile
 constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)

@@ -13,23 +13,26 @@
 //   bucket_kernel  one work-group: per-expert counts and offsets, the stable
 //                  token->expert order, each slot's token and weight, and the
 //                  per-expert work-item prefixes of the gemm lists.
-//   gemm_kernel<0> gate and up of (expert, 32-row tile, token group) items:
-//                  bit-plane unpack + LUT dequant into MFMA A fragments, MFMA
-//                  32x32x16 fp16 with fp32 accumulation, SwiGLU -> act (fp16).
-//   gemm_kernel<1> down of (expert, 64-row tile, K-piece, token group) items,
-//                  scaled by the routing weight and atomically added into y.
+//   expert_kernel  persistent, one launch per token-tile size: gate and up of
+//                  (expert, 32-row tile, token group) items (bit-plane unpack +
+//                  LUT dequant into MFMA A fragments, MFMA 16x16x32 fp16 with
+//                  fp32 accumulation, SwiGLU -> act fp16), then down of (expert,
+//                  64-row tile, K-piece, token group) items scaled by the
+//                  routing weight and atomically added into y; a down item waits
+//                  on a counter until its expert's act rows are complete.
 //   residual_kernel  x_next = fp16_rne(x + y) when requested.
 //
-// Dequantisation (the hot loop). Lane (r, g) of a wave owns row r (0..31) of the
-// item and a 128-column half g of each 256-column chunk. For one 32-column dword
-// of each of the b planes, a three-stage bit-matrix transpose (8x8 per byte)
-// turns the b plane words into eight index words W_i whose byte k is the b-bit
-// index of column 8k+i. One v_perm per weight drops that byte into an LDS
-// address, and one 16-bit LDS read fetches the fp16 weight from the LUT stripe:
-// dword (idx*64 + r) holds the two row-sets' LUT entries of row r (low/high
-// half), so each half-wave of 32 lanes hits 32 distinct banks. Eight looked-up
-// weights form one MFMA A operand; the B operand (activations) is stored with
-// the same in-group column permutation, so the contraction is unchanged.
+// Dequantisation (the hot loop). Lane (r, kg) of a wave owns row r (0..15) of
+// its 16-row half of the item and 128 columns (bytes 16*kg of a 64-byte
+// half-line) of each plane line. For one 32-column dword of each of the b
+// planes, a three-stage bit-matrix transpose (8x8 per byte) turns the plane
+// words into eight index words W_i whose byte k is the b-bit index of column
+// 8k+i. One v_perm per weight drops that byte into an LDS address, and one
+// 16-bit LDS read fetches the fp16 weight from the LUT stripe (dword idx*64 +
+// slot holds the two row-sets' entries of one row, low/high half; two copies
+// so each half-wave hits 32 distinct banks). Eight looked-up weights form one
+// MFMA A operand; the B operand (activations) is stored with the same in-group
+// column permutation, so the contraction is unchanged.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -563,6 +566,10 @@ __device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* ti
     }
 }
 
+// Waits until every vector-memory operation this wave issued has completed
+// (s_waitcnt vmcnt(0); gfx9 encoding, other counters left at their maximum).
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int dw) {
     return dw == 0 ? q.x : dw == 1 ? q.y : dw == 2 ? q.z : q.w;
 }
@@ -571,6 +578,8 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int dw) {
 
 // One work item of a list, decoded from its index.
 struct Item {
+    int mode;                 // 0 gate_up, 1 down
+    int pos, piece;           // list position (0 = shared expert when present), K-piece
     int ex, tile, grp;        // expert (E = shared), row tile, token group
     int n_tok, tbase, nl;     // tokens of the expert, first token of the group, tokens here
     int K, R;                 // columns / rows of the block
@@ -616,6 +625,8 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     }
     lo = __builtin_amdgcn_readfirstlane(lo);   // uniform: keep the item in scalar registers
     Item it;
+    it.mode = MODE;
+    it.pos = lo;
     const bool sh = p.has_shared && lo == 0;
     it.ex = sh ? p.E : lo - p.has_shared;
     const int tiles = sh ? p.tiles_s : p.tiles_r;
@@ -624,6 +635,7 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     it.tile = local % tiles;
     const int piece = (local / tiles) % pieces;
     it.grp = local / tiles / pieces;
+    it.piece = piece;
     it.n_tok = sh ? p.T : kconst(p.ws.counts)[it.ex];
     it.tbase = it.grp * 16 * NT;
     it.nl = min(16 * NT, it.n_tok - it.tbase);
@@ -645,13 +657,15 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     return it;
 }
 
-// LDS of the gemm kernels: a 64 KiB LUT stripe whose 256-byte row idx holds, in
+// LDS of the expert kernel: a 64 KiB LUT stripe whose 256-byte row idx holds, in
 // dword 32*h + 16*c + r, the LUT entry idx of item row 16*h + r (low half: set
 // 0, high half: set 1), in two copies c so that the 32 lanes of a half-wave
 // (rows r, copies kg & 1) hit 32 distinct banks; then the cross-wave partial
-// sums, the token rows of two items (double buffer) and the work-list prefix.
+// sums, the token rows of two items (double buffer), the work-list prefixes of
+// the gate_up and down lists, and one flag.
 constexpr int kStripeBytes = 65536;
 constexpr int kTokWords = 3 * 64;   // brow, orow, weight bits of up to 64 tokens
+constexpr int kPreWords = PW_MAX_EXPERTS + 2;   // work-list prefix of one list
 
 __device__ __forceinline__ int stripe_slot(int row) {   // copy 0 of item row 0..31
     return ((row >> 4) << 5) + (row & 15);
@@ -714,8 +728,9 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
     }
 }
 
-// Persistent work-group of 4 waves over the items of one list. An item is 32
-// rows of each of two row-sets over the item's K range, read as 128-byte lines
+// Persistent work-group of 4 waves over one gate_up list followed by the down
+// list of the same token-tile size, in one launch. An item is 32 rows of each of
+// two row-sets over the item's K range, read as 128-byte lines
 // (1024 columns of a plane row): wave q owns rows 16*(q >> 1) .. +15 of the
 // item and half-line q & 1 of every line, and lane (r, kg) of it loads 16
 // bytes (128 columns) of row r. A load instruction so covers 16 rows x 64
@@ -726,9 +741,19 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 // registers 2, 3. Items are assigned round-robin, so the next item's metadata
 // is known while the current one runs: its first chunk and LUT rows load
 // during the current item's last chunk.
-// MODE 0: gate_up, MODE 1: down. NT: token tiles of 16.
-template <int MODE, int NT>
-__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p) {
+//
+// Gate_up items come first in the combined order (index i < n_gu), down items
+// after them. A down item reads the act rows of its expert's K-piece, so it
+// waits until every gate_up item of that (list position, piece) has released
+// its act stores (agent-scope release, then a counter increment; the down item
+// spins on the counter and then acquires). Every dependency points to an
+// earlier index of the combined order and each work-group runs its items in
+// increasing order, so with all work-groups resident (the launch sizes the grid
+// to the occupancy) the earliest unfinished item never waits: no deadlock. The
+// last work-group to finish zeroes the counters for the next launch.
+// NT: token tiles of 16 per item.
+template <int NT>
+__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     // tid, r, kg are re-declared opaque at every item (below) so that the
     // compiler recomputes values derived from them instead of keeping dozens of
@@ -737,237 +762,281 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void gemm_kernel(GemmParams p
     const int q = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
     const int rh = q >> 1, kh = q & 1;
     int r = tid & 15, kg = (tid >> 4) & 3;
-    uint32_t* stripe = (uint32_t*)smem;
     float* red = (float*)(smem + kStripeBytes);                  // [4 waves][NT][4][64]
     int* s_tok = (int*)(red + 4 * NT * 4 * 64);                  // [2][kTokWords]
-    int* s_pre = s_tok + 2 * kTokWords;
-    const int npos = p.E + p.has_shared;
-    // Work-group w takes items w, w + G, w + 2G, ... of the list (G = grid size):
-    // no shared counter, and the next item is always known in advance.
-    for (int i = tid; i <= npos; i += 256) s_pre[i] = p.ws.prefix[p.list * (p.E + 2) + i];
-    __syncthreads();
-    const int n_items = __builtin_amdgcn_readfirstlane(s_pre[npos]);
-    int item = blockIdx.x;
-    if (item >= n_items) return;
-
-    const uint16_t* Bbase = MODE == 0 ? p.ws.xperm : p.ws.act;
-    const int ldb = MODE == 0 ? p.d : p.ld_act;
-    const __amdgpu_buffer_rsrc_t brsrc = make_rsrc(Bbase, p.b_bytes);
-
-    uint4 pa0[8], pa1[8], pb0[8], pb1[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pa0[i] = pa1[i] = pb0[i] = pb1[i] = make_uint4(0, 0, 0, 0);
-
-    // first column of this lane's 128 columns in chunk ch (relative to the item's K range)
-    auto lane_col = [&](int ch) { return ch * 1024 + kh * 512 + kg * 128; };
-    // plane loads of chunk ch (line ch of the item's K range) into (c0, c1):
-    // slot i holds plane i - (8 - b); absent planes and columns past the range read zeros
-    auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
-        const int Kb = it.K >> 3;
-        const bool vg = lane_col(ch) < it.klen;
-        const uint32_t nrec = (uint32_t)(it.R * Kb);
-        const int cb = (it.kbase + lane_col(ch)) >> 3;
-        const int row = rh * 16 + r;
-        const uint32_t off0 = vg ? (uint32_t)((it.rows0 + row) * Kb + cb) : kOOB;
-        const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
-        const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
-            c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
-        }
-    };
-    auto n_chunks = [](const Item& it) { return (it.klen + 1023) >> 10; };
-    auto lut_load = [&](const Item& it, LutStage& st) {
-        const int b0 = it.blk0->bits, b1 = it.blk1->bits;
-        lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
-                       (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
-    };
-    auto publish_item = [&](const Item& it, const LutStage& st, const TokInfo& tk, int par) {
-        if (tid < it.nl) {
-            int* tb = s_tok + par * kTokWords;
-            tb[tid] = tk.brow;
-            tb[64 + tid] = tk.orow;
-            tb[128 + tid] = __float_as_int(tk.w);
-        }
-        lut_stage_write(smem, st, it.blk0->bits, it.blk1->bits, tid);
-    };
-
-    Item it = decode_item<MODE, NT>(p, s_pre, npos, item);
-    {
-        LutStage st;
-        const TokInfo tk = fetch_tokinfo<MODE>(p, it, tid);
-        load_chunk(it, 0, pa0, pa1);
-        lut_load(it, st);
-        publish_item(it, st, tk, 0);
+    int* s_pre = s_tok + 2 * kTokWords;                          // [2][kPreWords]: gate_up, down
+    int* s_flag = s_pre + 2 * kPreWords;
+    const GemmParams& g = p.gu;                                  // fields common to both lists
+    uint32_t* const dep = g.ws.dep;
+    const int dstride = g.ws.dep_stride;
+    const int npos = g.E + g.has_shared;
+    // Work-group w takes items w, w + G, w + 2G, ... of the combined order (G =
+    // grid size): no shared counter, and the next item is always known.
+    for (int i = tid; i <= npos; i += 256) {
+        s_pre[i] = g.ws.prefix[p.gu.list * (g.E + 2) + i];
+        s_pre[kPreWords + i] = g.ws.prefix[p.dn.list * (g.E + 2) + i];
     }
     __syncthreads();
-    int par = 0;
+    const int n_gu = __builtin_amdgcn_readfirstlane(s_pre[npos]);
+    const int n_items = n_gu + __builtin_amdgcn_readfirstlane(s_pre[kPreWords + npos]);
+    int item = blockIdx.x;
+    auto decode = [&](int i) -> Item {
+        return i < n_gu ? decode_item<0, NT>(p.gu, s_pre, npos, i)
+                        : decode_item<1, NT>(p.dn, s_pre + kPreWords, npos, i - n_gu);
+    };
+    auto tokinfo = [&](const Item& it) -> TokInfo {
+        return it.mode == 0 ? fetch_tokinfo<0>(p.gu, it, tid) : fetch_tokinfo<1>(p.dn, it, tid);
+    };
 
-    while (true) {
-        asm volatile("" : "+v"(tid), "+v"(r), "+v"(kg));
-        const int nch = n_chunks(it);
-        const int ntl = (it.nl + 15) >> 4;
-        const int* tb = s_tok + par * kTokWords;
-        // the next item: its metadata and token rows now
-        const int next = item + (int)gridDim.x;
-        const bool has_next = next < n_items;
-        Item nit = it;
-        TokInfo ntk{0, 0, 0.0f};
-        if (has_next) {
-            nit = decode_item<MODE, NT>(p, s_pre, npos, next);
-            ntk = fetch_tokinfo<MODE>(p, nit, tid);
-        }
+    if (item < n_items) {
 
-        uint32_t boff[NT];
-        bool bok[NT];
+        uint4 pa0[8], pa1[8], pb0[8], pb1[8];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int i = nt * 16 + r;
-            bok[nt] = i < it.nl;
-            boff[nt] = bok[nt] ? (uint32_t)(tb[i] * ldb + kh * 512 + kg * 128) : 0u;
-        }
-        floatx4 acc0[NT], acc1[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            acc0[nt] = (floatx4)0.0f;
-            acc1[nt] = (floatx4)0.0f;
-        }
+        for (int i = 0; i < 8; ++i) pa0[i] = pa1[i] = pb0[i] = pb1[i] = make_uint4(0, 0, 0, 0);
 
-        auto load_b = [&](int ch, int dw, half8 (&bf)[NT][4], bool vg) {
+        // first column of this lane's 128 columns in chunk ch (relative to the item's K range)
+        auto lane_col = [&](int ch) { return ch * 1024 + kh * 512 + kg * 128; };
+        // plane loads of chunk ch (line ch of the item's K range) into (c0, c1):
+        // slot i holds plane i - (8 - b); absent planes and columns past the range read zeros
+        auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
+            const int Kb = it.K >> 3;
+            const bool vg = lane_col(ch) < it.klen;
+            const uint32_t nrec = (uint32_t)(it.R * Kb);
+            const int cb = (it.kbase + lane_col(ch)) >> 3;
+            const int row = rh * 16 + r;
+            const uint32_t off0 = vg ? (uint32_t)((it.rows0 + row) * Kb + cb) : kOOB;
+            const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
+            const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const uint32_t off =
-                    (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 1024 + 32 * dw)) * 2u : kOOB;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) bf[nt][m] = __builtin_bit_cast(half8, buf_load16(brsrc, off + 16u * m));
+            for (int i = 0; i < 8; ++i) {
+                c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
+                c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
             }
         };
+        auto n_chunks = [](const Item& it) { return (it.klen + 1023) >> 10; };
+        auto lut_load = [&](const Item& it, LutStage& st) {
+            const int b0 = it.blk0->bits, b1 = it.blk1->bits;
+            lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
+                           (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
+        };
+        auto publish_item = [&](const Item& it, const LutStage& st, const TokInfo& tk, int par) {
+            if (tid < it.nl) {
+                int* tb = s_tok + par * kTokWords;
+                tb[tid] = tk.brow;
+                tb[64 + tid] = tk.orow;
+                tb[128 + tid] = __float_as_int(tk.w);
+            }
+            lut_stage_write(smem, st, it.blk0->bits, it.blk1->bits, tid);
+        };
 
-        const uint32_t slot = lds_addr(smem) + (uint32_t)((rh * 32 + (kg & 1) * 16 + r) * 4);
-        // One chunk: for each of the lane's four 32-column dwords, transpose the
-        // plane words of both sets, look the weights up and feed the MFMAs. The B
-        // fragments of a dword (L2-resident activations) load at its start and
-        // arrive while the transposes and lookups run. Lanes past K hold zero B
-        // fragments, so their A fragments need no masking. A wave whose half of
-        // the chunk lies wholly past K skips it.
-        auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
-            if (ch * 1024 + kh * 512 >= it.klen) return;
-            const bool vg = lane_col(ch) < it.klen;
-            half8 bfr[NT][4];
+        Item it = decode(item);
+        {
+            LutStage st;
+            const TokInfo tk = tokinfo(it);
+            load_chunk(it, 0, pa0, pa1);
+            lut_load(it, st);
+            publish_item(it, st, tk, 0);
+        }
+        __syncthreads();
+        int par = 0;
+
+        while (true) {
+            asm volatile("" : "+v"(tid), "+v"(r), "+v"(kg));
+            const int nch = n_chunks(it);
+            const int ntl = (it.nl + 15) >> 4;
+            const int* tb = s_tok + par * kTokWords;
+            // B operand: xperm rows (gate_up) or act rows (down)
+            const int ldb = it.mode == 0 ? g.d : g.ld_act;
+            const __amdgpu_buffer_rsrc_t brsrc =
+                it.mode == 0 ? make_rsrc(g.ws.xperm, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
+            if (it.mode == 1) {
+                // every gate_up item of this expert's K-piece has released its act rows
+                const uint32_t need = (uint32_t)((it.klen >> 5) * ((it.n_tok + 16 * NT - 1) / (16 * NT)));
+                const uint32_t* c = dep + it.pos * dstride + it.piece;
+                while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need)
+                    __builtin_amdgcn_s_sleep(1);
+            }
+            // the next item: its metadata and token rows now
+            const int next = item + (int)gridDim.x;
+            const bool has_next = next < n_items;
+            Item nit = it;
+            TokInfo ntk{0, 0, 0.0f};
+            if (has_next) {
+                nit = decode(next);
+                ntk = tokinfo(nit);
+            }
+
+            uint32_t boff[NT];
+            bool bok[NT];
 #pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-                load_b(ch, dw, bfr, vg);
-                uint32_t w0[8], w1[8], rw0[8], rw1[8];
+            for (int nt = 0; nt < NT; ++nt) {
+                const int i = nt * 16 + r;
+                bok[nt] = i < it.nl;
+                boff[nt] = bok[nt] ? (uint32_t)(tb[i] * ldb + kh * 512 + kg * 128) : 0u;
+            }
+            floatx4 acc0[NT], acc1[NT];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    w0[i] = word_of(c0[i], dw);
-                    w1[i] = word_of(c1[i], dw);
+            for (int nt = 0; nt < NT; ++nt) {
+                acc0[nt] = (floatx4)0.0f;
+                acc1[nt] = (floatx4)0.0f;
+            }
+
+            auto load_b = [&](int ch, int dw, half8 (&bf)[NT][4], bool vg) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint32_t off =
+                        (bok[nt] && vg) ? (boff[nt] + (uint32_t)(it.kbase + ch * 1024 + 32 * dw)) * 2u : kOOB;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) bf[nt][m] = __builtin_bit_cast(half8, buf_load16(brsrc, off + 16u * m));
                 }
-                slots_to_indices(w0, rw0);
-                slots_to_indices(w1, rw1);
+            };
+
+            const uint32_t slot = lds_addr(smem) + (uint32_t)((rh * 32 + (kg & 1) * 16 + r) * 4);
+            // One chunk: for each of the lane's four 32-column dwords, transpose the
+            // plane words of both sets, look the weights up and feed the MFMAs. The B
+            // fragments of a dword (L2-resident activations) load at its start and
+            // arrive while the transposes and lookups run. Lanes past K hold zero B
+            // fragments, so their A fragments need no masking. A wave whose half of
+            // the chunk lies wholly past K skips it.
+            auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
+                if (ch * 1024 + kh * 512 >= it.klen) return;
+                const bool vg = lane_col(ch) < it.klen;
+                half8 bfr[NT][4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const half8 a0 = lut_fragment(rw0, m, slot, 0);
-                    const half8 a1 = lut_fragment(rw1, m, slot, 2);
+                for (int dw = 0; dw < 4; ++dw) {
+                    load_b(ch, dw, bfr, vg);
+                    uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        if (nt < ntl) {
-                            acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[nt][m], acc0[nt], 0, 0, 0);
-                            acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[nt][m], acc1[nt], 0, 0, 0);
+                    for (int i = 0; i < 8; ++i) {
+                        w0[i] = word_of(c0[i], dw);
+                        w1[i] = word_of(c1[i], dw);
+                    }
+                    slots_to_indices(w0, rw0);
+                    slots_to_indices(w1, rw1);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const half8 a0 = lut_fragment(rw0, m, slot, 0);
+                        const half8 a1 = lut_fragment(rw1, m, slot, 2);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            if (nt < ntl) {
+                                acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[nt][m], acc0[nt], 0, 0, 0);
+                                acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[nt][m], acc1[nt], 0, 0, 0);
+                            }
                         }
                     }
                 }
-            }
-        };
+            };
 
-        // chunks 0, 1, ... alternate between (pa, pb); chunk 0 arrived with the
-        // item. The next item's first chunk and LUT rows load into pa / st as soon
-        // as pa has been consumed for the last time.
-        LutStage st;
-        bool fetched = false;
-        auto fetch_next = [&]() {
-            if (has_next) {
-                load_chunk(nit, 0, pa0, pa1);
-                lut_load(nit, st);
-            }
-            fetched = true;
-        };
-        if (1 < nch) load_chunk(it, 1, pb0, pb1);
+            // chunks 0, 1, ... alternate between (pa, pb); chunk 0 arrived with the
+            // item. The next item's first chunk and LUT rows load into pa / st as soon
+            // as pa has been consumed for the last time.
+            LutStage st;
+            bool fetched = false;
+            auto fetch_next = [&]() {
+                if (has_next) {
+                    load_chunk(nit, 0, pa0, pa1);
+                    lut_load(nit, st);
+                }
+                fetched = true;
+            };
+            if (1 < nch) load_chunk(it, 1, pb0, pb1);
 #pragma unroll 1
-        for (int ch = 0; ch < nch; ch += 2) {
-            compute_chunk(ch, pa0, pa1);
-            if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
-            else if (ch + 1 < nch) fetch_next();
-            if (ch + 1 >= nch) break;
-            compute_chunk(ch + 1, pb0, pb1);
-            if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
-        }
-        if (!fetched) fetch_next();
+            for (int ch = 0; ch < nch; ch += 2) {
+                compute_chunk(ch, pa0, pa1);
+                if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
+                else if (ch + 1 < nch) fetch_next();
+                if (ch + 1 >= nch) break;
+                compute_chunk(ch + 1, pb0, pb1);
+                if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
+            }
+            if (!fetched) fetch_next();
 
-        // partner (other half-line) partial sums of the registers it finishes
-        const int pq = q ^ 1;
+            // partner (other half-line) partial sums of the registers it finishes
+            const int pq = q ^ 1;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt < ntl) {
-                float* w = red + ((q * NT + nt) * 4) * 64 + (tid & 63);
+            for (int nt = 0; nt < NT; ++nt) {
+                if (nt < ntl) {
+                    float* w = red + ((q * NT + nt) * 4) * 64 + (tid & 63);
+                    if (kh == 0) {
+                        w[0 * 64] = acc0[nt][2];
+                        w[1 * 64] = acc0[nt][3];
+                        w[2 * 64] = acc1[nt][2];
+                        w[3 * 64] = acc1[nt][3];
+                    } else {
+                        w[0 * 64] = acc0[nt][0];
+                        w[1 * 64] = acc0[nt][1];
+                        w[2 * 64] = acc1[nt][0];
+                        w[3 * 64] = acc1[nt][1];
+                    }
+                }
+            }
+            __syncthreads();   // every wave is done with the LUT stripe; partial sums visible
+            if (has_next) publish_item(nit, st, ntk, par ^ 1);
+
+            // sum of the two half-line partials of registers 2*kh, 2*kh+1 and the epilogue
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (nt >= ntl) break;
+                const int tok_i = nt * 16 + r;
+                const bool tv = tok_i < it.nl;
+                const float* pr = red + ((pq * NT + nt) * 4) * 64 + (tid & 63);
+                float g0, g1, u0, u1;
                 if (kh == 0) {
-                    w[0 * 64] = acc0[nt][2];
-                    w[1 * 64] = acc0[nt][3];
-                    w[2 * 64] = acc1[nt][2];
-                    w[3 * 64] = acc1[nt][3];
+                    g0 = acc0[nt][0]; g1 = acc0[nt][1]; u0 = acc1[nt][0]; u1 = acc1[nt][1];
                 } else {
-                    w[0 * 64] = acc0[nt][0];
-                    w[1 * 64] = acc0[nt][1];
-                    w[2 * 64] = acc1[nt][0];
-                    w[3 * 64] = acc1[nt][1];
+                    g0 = acc0[nt][2]; g1 = acc0[nt][3]; u0 = acc1[nt][2]; u1 = acc1[nt][3];
+                }
+                g0 += pr[0 * 64];
+                g1 += pr[1 * 64];
+                u0 += pr[2 * 64];
+                u1 += pr[3 * 64];
+                if (tv) {
+                    const int row = rh * 16 + kg * 4 + kh * 2;   // rows row, row+1 of the item
+                    const int orow = tb[64 + tok_i];
+                    if (it.mode == 0) {
+                        const float a0 = g0 / (1.0f + expf(-g0)) * u0;
+                        const float a1 = g1 / (1.0f + expf(-g1)) * u1;
+                        const int f = it.rows0 + row;   // even: f, f+1 are adjacent permuted columns
+                        const uint32_t pk = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
+                        // device-coherent store: written through to the memory side, so a down
+                        // item on another XCD that reads the row after the counter sees it
+                        __hip_atomic_store((uint32_t*)(g.ws.act + (size_t)orow * g.ld_act + (f & ~31) + perm32(f & 31)),
+                                           pk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        const float wv = __int_as_float(tb[128 + tok_i]);
+                        float* yr = g.y + (size_t)orow * g.d;
+                        unsafeAtomicAdd(yr + it.rows0 + row, wv * g0);
+                        unsafeAtomicAdd(yr + it.rows0 + row + 1, wv * g1);
+                        unsafeAtomicAdd(yr + it.rows1 + row, wv * u0);
+                        unsafeAtomicAdd(yr + it.rows1 + row + 1, wv * u1);
+                    }
                 }
             }
+            if (it.mode == 0) vm_drain();   // this wave's act stores are complete
+            __syncthreads();   // next item's LUT rows and token rows are in place; partials read
+            if (it.mode == 0 && tid == 0)
+                __hip_atomic_fetch_add(dep + it.pos * dstride + ((it.tile * 32) / kDownPiece), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (!has_next) break;
+            item = next;
+            it = nit;
+            par ^= 1;
         }
-        __syncthreads();   // every wave is done with the LUT stripe; partial sums visible
-        if (has_next) publish_item(nit, st, ntk, par ^ 1);
+    }
 
-        // sum of the two half-line partials of registers 2*kh, 2*kh+1 and the epilogue
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt >= ntl) break;
-            const int tok_i = nt * 16 + r;
-            const bool tv = tok_i < it.nl;
-            const float* pr = red + ((pq * NT + nt) * 4) * 64 + (tid & 63);
-            float g0, g1, u0, u1;
-            if (kh == 0) {
-                g0 = acc0[nt][0]; g1 = acc0[nt][1]; u0 = acc1[nt][0]; u1 = acc1[nt][1];
-            } else {
-                g0 = acc0[nt][2]; g1 = acc0[nt][3]; u0 = acc1[nt][2]; u1 = acc1[nt][3];
-            }
-            g0 += pr[0 * 64];
-            g1 += pr[1 * 64];
-            u0 += pr[2 * 64];
-            u1 += pr[3 * 64];
-            if (tv) {
-                const int row = rh * 16 + kg * 4 + kh * 2;   // rows row, row+1 of the item
-                const int orow = tb[64 + tok_i];
-                if (MODE == 0) {
-                    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
-                    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
-                    const int f = it.rows0 + row;   // even: f, f+1 are adjacent permuted columns
-                    const uint32_t pk = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
-                    *(uint32_t*)(p.ws.act + (size_t)orow * p.ld_act + (f & ~31) + perm32(f & 31)) = pk;
-                } else {
-                    const float wv = __int_as_float(tb[128 + tok_i]);
-                    float* yr = p.y + (size_t)orow * p.d;
-                    unsafeAtomicAdd(yr + it.rows0 + row, wv * g0);
-                    unsafeAtomicAdd(yr + it.rows0 + row + 1, wv * g1);
-                    unsafeAtomicAdd(yr + it.rows1 + row, wv * u0);
-                    unsafeAtomicAdd(yr + it.rows1 + row + 1, wv * u1);
-                }
-            }
-        }
-        __syncthreads();   // next item's LUT rows and token rows are in place; partials read
-        if (!has_next) break;
-        item = next;
-        it = nit;
-        par ^= 1;
+    // the last work-group to finish zeroes the dependency counters
+    __syncthreads();
+    if (tid == 0) {
+        vm_drain();   // this work-group's counter increments (thread 0's) are performed
+        const uint32_t prev = __hip_atomic_fetch_add(dep + (size_t)npos * dstride, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == gridDim.x - 1u;
+    }
+    __syncthreads();
+    if (*s_flag) {
+        for (int i = tid; i <= npos * dstride; i += 256)
+            __hip_atomic_store(dep + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -979,8 +1048,9 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
     if (i < n) out[i] = f2h(h2f(x[i]) + y[i]);
 }
 
-__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws) {
+__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_dep) {
     if (threadIdx.x == 0) *ws.status = 0u;
+    for (int i = threadIdx.x; i < n_dep; i += 64) ws.dep[i] = 0u;
 }
 
 struct DebugParams {
@@ -1047,13 +1117,13 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
 
 // ============================================================================ launchers
 
-int gemm_lds_bytes(int tile_tokens) {
+int expert_lds_bytes(int tile_tokens) {
     const int nt = tile_tokens / 16;
-    return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + (PW_MAX_EXPERTS + 2) * 4;
+    return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + 2 * kPreWords * 4 + 16;
 }
 
-hipError_t launch_init_ws(const Workspace& ws, hipStream_t s) {
-    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws);
+hipError_t launch_init_ws(const Workspace& ws, int n_dep, hipStream_t s) {
+    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws, n_dep);
     return hipGetLastError();
 }
 
@@ -1067,27 +1137,36 @@ hipError_t launch_bucket(const BucketParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE, int NT>
-static hipError_t launch_gemm_t(const GemmParams& p, int lds_bytes, int n_wg, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)gemm_kernel<MODE, NT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+// Resident work-groups per CU of expert_kernel<NT> (0 if it cannot run).
+template <int NT>
+static hipError_t expert_occupancy(int* per_cu) {
+    static int cached = -1;
+    if (cached < 0) {
+        const void* f = (const void*)expert_kernel<NT>;
+        hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (err != hipSuccess) return err;
-        attr_set = true;
+        int n = 0;
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, expert_lds_bytes(16 * NT));
+        if (err != hipSuccess) return err;
+        cached = n < (NT == 1 ? 2 : 1) ? n : (NT == 1 ? 2 : 1);
     }
-    hipLaunchKernelGGL((gemm_kernel<MODE, NT>), dim3(n_wg), dim3(256), lds_bytes, s, p);
+    *per_cu = cached;
+    return hipSuccess;
+}
+
+template <int NT>
+static hipError_t launch_experts_t(const ExpertParams& p, int n_cu, hipStream_t s) {
+    int per_cu = 0;
+    hipError_t err = expert_occupancy<NT>(&per_cu);
+    if (err != hipSuccess) return err;
+    if (per_cu < 1) return hipErrorLaunchOutOfResources;
+    // every work-group resident at once: the dependency waits rely on it
+    hipLaunchKernelGGL((expert_kernel<NT>), dim3(per_cu * n_cu), dim3(256), expert_lds_bytes(16 * NT), s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int mode, int tile_tokens, const GemmParams& p, int lds_bytes, int n_wg,
-                       hipStream_t s) {
-    if (mode == 0) {
-        return tile_tokens == kSmallTokens ? launch_gemm_t<0, 1>(p, lds_bytes, n_wg, s)
-                                           : launch_gemm_t<0, 4>(p, lds_bytes, n_wg, s);
-    }
-    return tile_tokens == kSmallTokens ? launch_gemm_t<1, 1>(p, lds_bytes, n_wg, s)
-                                       : launch_gemm_t<1, 4>(p, lds_bytes, n_wg, s);
+hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {
+    return tile_tokens == kSmallTokens ? launch_experts_t<1>(p, n_cu, s) : launch_experts_t<4>(p, n_cu, s);
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,

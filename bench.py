@@ -31,7 +31,7 @@ def log(*a):
 
 
 KERNEL_SRC = os.path.join(ROOT, "any_precision_bit_amd", "csrc", "pw_kernels.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_gate_up_c1_decode_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_kernel_c1_decode_traffic.md")
 
 
 def kernel_code_digest():
@@ -42,7 +42,7 @@ def kernel_code_digest():
 
 
 def measured_traffic():
-    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary
+    """HBM bytes per expert-kernel launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE runs, scaled by a 1 GiB copy's readings), or None
     when the kernel code has changed since those counters were taken."""
     try:
@@ -145,7 +145,7 @@ def main():
     ran = min(len(clones), max(args.warmup, args.steps))   # clones that have run a forward
     n_rep = max(args.steps // 2, ran)
     avg_ms = []
-    for phase in range(3):
+    for phase in range(2):   # 0 routing, 1 experts
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(n_rep):
@@ -153,23 +153,24 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         avg_ms.append(e0.elapsed_time(e1) / n_rep)
-    nbytes = clones[0]["lay"].last_bytes(stream)
-    names = ["routing", "gate_up", "down"]
-    for i in range(3):
-        gbs = nbytes[i] / (avg_ms[i] * 1e-3) / 1e9 if avg_ms[i] > 0 else 0.0
-        log(f"  {names[i]:8s} {avg_ms[i] * 1e3:8.2f} us  {nbytes[i] / 1e6:8.2f} MB  {gbs:8.1f} GB/s")
-    layer_bytes = nbytes[0] + nbytes[1] + nbytes[2]
+    nb = clones[0]["lay"].last_bytes(stream)   # route, gate_up, down, residual
+    phase_bytes = [nb[0], nb[1] + nb[2]]
+    names = ["routing", "experts"]
+    for i in range(2):
+        gbs = phase_bytes[i] / (avg_ms[i] * 1e-3) / 1e9 if avg_ms[i] > 0 else 0.0
+        log(f"  {names[i]:8s} {avg_ms[i] * 1e3:8.2f} us  {phase_bytes[i] / 1e6:8.2f} MB  {gbs:8.1f} GB/s")
+    layer_bytes = nb[0] + nb[1] + nb[2]
     layer_gbs = layer_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step {ms_per_step * 1e3:.2f} us (phases sum {sum(avg_ms) * 1e3:.2f} us), layer bytes "
         f"{layer_bytes / 1e6:.1f} MB -> {layer_gbs:.0f} GB/s ({layer_gbs / HBM_PEAK_GBS:.1%} of HBM peak); "
         f"wall {wall:.3f}s")
 
-    # dominant kernel: gate_up (about two thirds of the layer's bytes)
-    gu_gbs = nbytes[1] / (avg_ms[1] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "gemm_kernel<0,1> (gate_up + SwiGLU)",
-                "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "bytes_per_launch": nbytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3)}
+    # dominant kernel: the expert kernel (gate_up + SwiGLU + down, >99 % of the layer's bytes)
+    ex_gbs = phase_bytes[1] / (avg_ms[1] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "expert_kernel<1> (gate_up + SwiGLU + down + accumulation)",
+                "achieved": round(ex_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ex_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "bytes_per_launch": phase_bytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -149,10 +149,11 @@ pw_status pw_layer_status(pw_layer layer, void* stream, uint32_t* flags);
 
 /* Measurement hook: enqueues again, on `stream`, the kernels of one phase of
  * this layer's last forward with the same arguments: 0 routing (router + bucket
- * sort), 1 gate_up + SwiGLU, 2 down + weighted accumulation, 3 residual. Used to
- * time one phase alone; the buffers of that forward must still be alive. The
- * phase rewrites its outputs (phase 0 zeroes y, phase 2 adds into y again), so
- * y is meaningful only after a full forward. PW_E_STATE before any forward. */
+ * sort), 1 experts (one kernel per token-tile size: gate_up + SwiGLU, then down
+ * + weighted accumulation), 2 residual. Used to time one phase alone; the
+ * buffers of that forward must still be alive. The phase rewrites its outputs
+ * (phase 0 zeroes y, phase 1 adds into y again), so y is meaningful only after
+ * a full forward. PW_E_STATE before any forward; PW_E_ARG for another phase. */
 pw_status pw_moe_replay(pw_layer layer, int32_t phase, void* stream);
 
 /* Algorithmic bytes of the last forward's kernels, computed on the host from
