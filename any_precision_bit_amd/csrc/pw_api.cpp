@@ -96,7 +96,6 @@ struct pw_layer_s {
     // launch record of the last forward (for pw_layer_last_bytes and pw_moe_replay)
     int last_T = 0;
     pw::RouteParams rp{};
-    pw::BucketParams bp{};
     pw::GemmParams gp_gu{}, gp_dn{};
     const uint16_t* res_x = nullptr;
     const float* res_y = nullptr;
@@ -150,9 +149,12 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
     const size_t o_st = off;     off += al(sizeof(uint32_t));
+    const size_t o_apx = off;    off += al(sizeof(float) * (size_t)T * E);
+    const size_t o_bnd = off;    off += al(sizeof(float) * (size_t)T * E);
     const int dep_stride = (L->f_max + pw::kDownPiece - 1) / pw::kDownPiece;
     const int n_dep = (E + 1) * dep_stride + 1;
-    const size_t o_dep = off;    off += al(sizeof(uint32_t) * (size_t)n_dep);
+    const int n_counters = n_dep + T + 1;   // dep, tok_cnt, route_done
+    const size_t o_dep = off;    off += al(sizeof(uint32_t) * (size_t)n_counters);
     hipError_t e;
     int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess)
@@ -180,7 +182,11 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
+    L->ws.apx = (float*)(b + o_apx);
+    L->ws.bnd = (float*)(b + o_bnd);
     L->ws.dep = (uint32_t*)(b + o_dep);
+    L->ws.tok_cnt = L->ws.dep + n_dep;
+    L->ws.route_done = L->ws.tok_cnt + T;
     L->ws.dep_stride = dep_stride;
     for (int i = 0; i < kStageSlots; ++i) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
@@ -191,7 +197,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess)
             return hip_fail(e, "hipEventCreate");
     }
-    if ((e = pw::launch_init_ws(L->ws, n_dep, s)) != hipSuccess) return hip_fail(e, "init workspace");
+    if ((e = pw::launch_init_ws(L->ws, n_counters, s)) != hipSuccess) return hip_fail(e, "init workspace");
     L->dev_ready = true;
     return PW_OK;
 }
@@ -232,7 +238,6 @@ pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
     switch (phase) {
         case 0:
             if ((e = pw::launch_route(L->rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
-            if ((e = pw::launch_bucket(L->bp, s)) != hipSuccess) return hip_fail(e, "bucket kernel");
             break;
         case 1: {
             pw::ExpertParams ep{L->gp_gu, L->gp_dn};
@@ -400,24 +405,18 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     rp.k = k;
     rp.ws = L->ws;
     rp.y = y;
-    pw::BucketParams& bp = L->bp;
-    bp = pw::BucketParams{};
-    bp.T = T;
-    bp.E = E;
-    bp.k = k;
-    bp.has_shared = has_shared;
-    bp.tiles_gu_r = D.d_ffn / 32;
-    bp.tiles_gu_s = D.d_ffn_shared / 32;
-    bp.tiles_dn = d / 64;
-    bp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
-    bp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
-    bp.ws = L->ws;
+    rp.has_shared = has_shared;
+    rp.tiles_gu_r = D.d_ffn / 32;
+    rp.tiles_gu_s = D.d_ffn_shared / 32;
+    rp.tiles_dn = d / 64;
+    rp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
+    rp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
     if (route) {
         rp.o_ids = route->topk_ids;
         rp.o_w = route->topk_w;
-        bp.o_counts = route->expert_count;
-        bp.o_offsets = route->expert_offset;
-        bp.o_sorted = route->sorted_assign;
+        rp.o_counts = route->expert_count;
+        rp.o_offsets = route->expert_offset;
+        rp.o_sorted = route->sorted_assign;
     }
     pw::GemmParams gp{};
     gp.blocks = L->d_blocks;
@@ -442,8 +441,8 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     L->gp_dn = gp;
     L->gp_dn.tiles_r = d / 64;
     L->gp_dn.tiles_s = has_shared ? d / 64 : 0;
-    L->gp_dn.pieces_r = bp.pieces_dn_r;
-    L->gp_dn.pieces_s = has_shared ? bp.pieces_dn_s : 1;
+    L->gp_dn.pieces_r = rp.pieces_dn_r;
+    L->gp_dn.pieces_s = has_shared ? rp.pieces_dn_s : 1;
     L->gp_dn.b_bytes = (uint32_t)(((size_t)D.max_tokens * k + (size_t)D.max_tokens * has_shared) * L->f_max * 2);
     L->res_x = (const uint16_t*)x;
     L->res_y = y;

@@ -36,8 +36,13 @@ struct Workspace {
     uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
+    float* apx;          // [max_T][E]   fp32 router logits (route kernel, between work-groups)
+    float* bnd;          // [max_T][E]   their sum |x w| bounds
+    // counters, contiguous and zeroed once; every launch leaves them at zero
     uint32_t* dep;       // [(E+1)*dep_stride + 1]  gate_up items done per (list position, down
                          //              K-piece); last word: work-groups finished (expert kernel)
+    uint32_t* tok_cnt;   // [max_T]      route work-groups finished per token
+    uint32_t* route_done;// [1]          tokens finished (route kernel)
     int dep_stride;      // down K-pieces of the widest expert
 };
 
@@ -46,17 +51,13 @@ struct RouteParams {
     const uint16_t* wr;
     const uint16_t* bias;  // may be null
     int T, d, E, k;
+    int has_shared;
+    int tiles_gu_r, tiles_gu_s, tiles_dn;   // row tiles per item list
+    int pieces_dn_r, pieces_dn_s;           // K-pieces of a routed / the shared down item
     Workspace ws;
     float* y;              // zeroed here
     int32_t* o_ids;        // optional caller copies of the routing outputs
     float* o_w;
-};
-
-struct BucketParams {
-    int T, E, k, has_shared;
-    int tiles_gu_r, tiles_gu_s, tiles_dn;   // row tiles per item list
-    int pieces_dn_r, pieces_dn_s;           // K-pieces of a routed / the shared down item
-    Workspace ws;
     int32_t* o_counts;
     int32_t* o_offsets;
     int32_t* o_sorted;
@@ -94,9 +95,8 @@ struct ExpertParams {
     GemmParams dn;
 };
 
-hipError_t launch_init_ws(const Workspace& ws, int n_dep, hipStream_t s);
+hipError_t launch_init_ws(const Workspace& ws, int n_counters, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
-hipError_t launch_bucket(const BucketParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
 // The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s);
@@ -111,8 +111,7 @@ int expert_lds_bytes(int tile_tokens);
 constexpr int kSmallTokens = 16;          // experts with 1..16 tokens: one 16-token MFMA tile
 constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
-constexpr int kRouteThreads = 512;
-constexpr int kBucketThreads = 1024;
+constexpr int kRouteThreads = 256;          // route kernel: 4 waves, one expert each
 constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)
 
 }  // namespace pw

@@ -6,13 +6,15 @@
 // and fuses routing, SwiGLU expert activation and weighted accumulation.
 //
 // Kernels, in stream order per forward:
-//   route_kernel   one work-group per token: fp32 router logits with an error
-//                  bound, exact int64 logits (units of 2^-48) for the candidates
-//                  the bound cannot rule out, exact top-k, softmax over the k
-//                  selected; also the column-permuted copy of x, and y = 0.
-//   bucket_kernel  one work-group: per-expert counts and offsets, the stable
-//                  token->expert order, each slot's token and weight, and the
-//                  per-expert work-item prefixes of the gemm lists.
+//   route_kernel   T * ceil(E/4) work-groups, one expert per wave: fp32 router
+//                  logits with an error bound; per token, the last work-group
+//                  recomputes the candidates the bound cannot rule out exactly
+//                  (int64, units of 2^-48) and takes the exact top-k and the
+//                  softmax over the k selected; the last token's work-group
+//                  sorts the assignments by expert (counts, offsets, stable
+//                  order, each slot's token and weight) and writes the
+//                  per-expert work-item prefixes. Also the column-permuted copy
+//                  of x, and y = 0.
 //   expert_kernel  persistent, one launch per token-tile size: gate and up of
 //                  (expert, 32-row tile, token group) items (bit-plane unpack +
 //                  LUT dequant into MFMA A fragments, MFMA 16x16x32 fp16 with
@@ -97,6 +99,11 @@ __device__ __forceinline__ int perm32(int c) {
 
 // ============================================================================ route
 
+// Waits until every vector-memory operation this wave issued has completed
+// (s_waitcnt vmcnt(0); gfx9 encoding, other counters left at their maximum).
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+
 __device__ __forceinline__ void add_pair(uint32_t xw, uint32_t ww, long long& acc, float& sab,
                                          int& bad) {
 #pragma unroll
@@ -118,82 +125,197 @@ __device__ __forceinline__ bool key_gt(V va, int ea, V vb, int eb) {
     return va > vb || (va == vb && ea < eb);
 }
 
-// fp32 logit and bound of every expert e = wave + NW*j of one token. Columns
-// come in blocks of 512 (8 per lane); a wave issues the weight rows of BATCH
-// experts together, then reads each block of x (fp32, in LDS) once and applies
-// it to all of them.
+// fp32 logit and bound of expert e for token t, one wave: lane l takes columns
+// l*8 + 512*i; products of two fp16 values are exact in fp32.
 template <int NB>
-__device__ __forceinline__ void approx_logits(const RouteParams& p, const float* s_xf, float* s_apx,
-                                              float* s_bnd, int wave, int lane) {
+__device__ __forceinline__ void approx_logit(const RouteParams& p, int t, int e, int lane, float& acc_out,
+                                             float& sab_out) {
+    const int d = p.d;
+    const uint16_t* xr = p.x + (size_t)t * d;
+    const uint16_t* wr = p.wr + (size_t)e * d;
+    uint4 xv[NB], wv[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int c = lane * 8 + 512 * i;
+        const bool ok = c < d;
+        xv[i] = ok ? *(const uint4*)(xr + c) : make_uint4(0, 0, 0, 0);
+        wv[i] = ok ? *(const uint4*)(wr + c) : make_uint4(0, 0, 0, 0);
+    }
+    float acc = 0.0f, sab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const uint32_t xa[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        const uint32_t wa[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const float xf = h2f((uint16_t)(xa[h >> 1] >> (16 * (h & 1))));
+            const float wf = h2f((uint16_t)(wa[h >> 1] >> (16 * (h & 1))));
+            acc = fmaf(xf, wf, acc);
+            sab = fmaf(fabsf(xf), fabsf(wf), sab);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        acc += __shfl_xor(acc, off);
+        sab += __shfl_xor(sab, off);
+    }
+    acc_out = acc;
+    sab_out = sab;
+}
+
+// Exclusive scan over the kRouteThreads threads; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
     constexpr int NW = kRouteThreads / 64;
-    constexpr int BATCH = NB >= 32 ? 1 : 32 / NB;
-    const int d = p.d, E = p.E;
-    for (int e0 = wave; e0 < E; e0 += NW * BATCH) {
-        uint4 w[BATCH][NB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = v;
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            const int e = e0 + NW * j;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) s_tmp[wave] = inc;
+    __syncthreads();
+    int before = 0, tot = 0;
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int c = lane * 8 + 512 * i;
-                w[j][i] = (e < E && c < d) ? *(const uint4*)(p.wr + (size_t)e * d + c) : make_uint4(0, 0, 0, 0);
-            }
+    for (int w = 0; w < NW; ++w) {
+        const int c = s_tmp[w];
+        before += w < wave ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return inc - v + before;
+}
+
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* a) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void store_agent(T* a, T v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stable counting sort of the T*k assignments by expert (counts, exclusive
+// offsets, assignments in ascending (t, j) order per expert, each slot's token
+// and weight) and the per-expert item prefix of each expert-kernel work list.
+// One work-group; ids and weights come from other work-groups of this launch.
+__device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s_run, int* s_wc, int* s_tmp) {
+    constexpr int NW = kRouteThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = p.E, n = p.T * p.k;
+    for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kRouteThreads) atomicAdd(&s_cnt[load_agent(p.ws.ids + i)], 1);
+    __syncthreads();
+    // exclusive offsets over experts (E <= kRouteThreads)
+    {
+        int tot;
+        const int v = tid < E ? s_cnt[tid] : 0;
+        const int ex = block_excl_scan(v, s_tmp, &tot);
+        if (tid < E) {
+            s_off[tid] = ex;
+            s_run[tid] = ex;
+            p.ws.counts[tid] = v;
+            p.ws.offsets[tid] = ex;
+            if (p.o_counts) p.o_counts[tid] = v;
+            if (p.o_offsets) p.o_offsets[tid] = ex;
         }
-        float acc[BATCH], sab[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) acc[j] = sab[j] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c = lane * 8 + 512 * i;
-            if (c >= d) break;
-            const float4 xa = *(const float4*)(s_xf + c), xb = *(const float4*)(s_xf + c + 4);
-            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const uint32_t wv[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
-#pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    // the product of two fp16 values is exact in fp32
-                    const float wf = h2f((uint16_t)(wv[h >> 1] >> (16 * (h & 1))));
-                    acc[j] = fmaf(xv[h], wf, acc[j]);
-                    sab[j] = fmaf(fabsf(xv[h]), fabsf(wf), sab[j]);
-                }
-            }
+        if (tid == 0) {
+            s_off[E] = tot;
+            p.ws.offsets[E] = tot;
+            if (p.o_offsets) p.o_offsets[E] = tot;
         }
+    }
+    __syncthreads();
+    // stable placement, kRouteThreads assignments at a time: lanes of one wave
+    // with the same expert find each other by matching the 8 id bits
+    for (int base = 0; base < n; base += kRouteThreads) {
+        for (int j = tid; j < NW * E; j += kRouteThreads) s_wc[j] = 0;
+        __syncthreads();
+        const int i = base + tid;
+        const bool valid = i < n;
+        const int e = valid ? load_agent(p.ws.ids + i) : 0;
+        unsigned long long same = __ballot(valid);
 #pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                acc[j] += __shfl_xor(acc[j], off);
-                sab[j] += __shfl_xor(sab[j], off);
-            }
+        for (int bit = 0; bit < 8; ++bit) {
+            const unsigned long long bb = __ballot(valid && ((e >> bit) & 1));
+            same &= ((e >> bit) & 1) ? bb : ~bb;
         }
-        if (lane == 0) {
-#pragma unroll
-            for (int j = 0; j < BATCH; ++j) {
-                const int e = e0 + NW * j;
-                if (e < E) {
-                    const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
-                    s_apx[e] = acc[j] + bf;
-                    s_bnd[e] = sab[j] + fabsf(bf);
-                }
+        const int rank = __popcll(same & __lanemask_lt());
+        if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kRouteThreads) {
+            int run = s_run[ee];
+            for (int w = 0; w < NW; ++w) {
+                const int c = s_wc[w * E + ee];
+                s_wc[w * E + ee] = run;
+                run += c;
             }
+            s_run[ee] = run;
         }
+        __syncthreads();
+        if (valid) {
+            const int pos = s_wc[wave * E + e] + rank;
+            p.ws.sorted[pos] = i;
+            p.ws.slot_tok[pos] = i / p.k;   // token of the slot, and its routing weight
+            p.ws.slot_w[pos] = load_agent(p.ws.w + i);
+            if (p.o_sorted) p.o_sorted[pos] = i;
+        }
+        __syncthreads();
+    }
+
+    // ---- work lists: list position 0 is the shared expert (long items first);
+    // E + 1 positions can exceed the thread count, so they are scanned in chunks
+    const int npos = E + p.has_shared;
+    const int stride = E + 2;
+    int carry[N_LISTS] = {0, 0, 0, 0};
+    for (int p0 = 0; p0 < npos; p0 += kRouteThreads) {
+        const int pos = p0 + tid;
+        int cnt = 0, tgu = 0, pdn = 1;
+        if (pos < npos) {
+            const bool sh = p.has_shared && pos == 0;
+            const int ex = sh ? E : pos - p.has_shared;
+            cnt = sh ? p.T : s_cnt[ex];
+            tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
+            pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
+        }
+        const int small = (cnt >= 1 && cnt <= kSmallTokens) ? 1 : 0;
+        const int groups = cnt > kSmallTokens ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
+        const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn,
+                                     groups * p.tiles_dn * pdn};
+#pragma unroll
+        for (int l = 0; l < N_LISTS; ++l) {
+            int tot;
+            const int ex = block_excl_scan(nitems[l], s_tmp, &tot);
+            if (pos < npos) p.ws.prefix[l * stride + pos] = carry[l] + ex;
+            carry[l] += tot;
+        }
+    }
+    if (tid == 0) {
+#pragma unroll
+        for (int l = 0; l < N_LISTS; ++l) p.ws.prefix[l * stride + npos] = carry[l];
     }
 }
 
-// One work-group per token. Selection is exact although the bulk of the logits
-// is computed in fp32: every fp32 logit A_e is within delta of the exact value
+// Routing in one launch of T * ceil(E/4) work-groups of 4 waves; work-group
+// (t, eb) computes, one expert per wave, the fp32 logits of experts 4*eb .. +3
+// for token t with an error bound. Selection is exact although the bulk of
+// the logits is fp32: every fp32 logit A_e is within delta of the exact value
 // L_e, so any expert of the exact top-k has A_e >= a_k - 2*delta, a_k being the
-// k-th largest A. Only those candidates are recomputed exactly (int64 in units
-// of 2^-48) and the top-k is taken over their exact values.
+// k-th largest A. The work-group that finishes token t last (a counter per
+// token) recomputes only those candidates exactly (int64, units of 2^-48),
+// takes the top-k over the exact values and the softmax over the k; the one
+// that finishes the last token does the bucket sort and the work lists.
+// Values passed between work-groups are device-coherent stores, drained before
+// the counter increment that publishes them, and device-coherent loads.
+template <int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     constexpr int NW = kRouteThreads / 64;
-    const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
-    __shared__ __align__(16) uint16_t s_x[kMaxModel];
-    __shared__ __align__(16) float s_xf[kMaxModel];
+    const int nb = (E + NW - 1) / NW;
+    const int t = blockIdx.x / nb, eb = blockIdx.x - t * nb;
     __shared__ float s_apx[PW_MAX_EXPERTS];
     __shared__ float s_bnd[PW_MAX_EXPERTS];
     __shared__ int s_cand[PW_MAX_EXPERTS];
@@ -202,34 +324,50 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __shared__ int s_sele[PW_MAX_TOP_K];
     __shared__ float s_tau;
     __shared__ int s_ncand;
+    __shared__ int s_last;
+    // bucket sort (last work-group only)
+    __shared__ int s_cnt[PW_MAX_EXPERTS];
+    __shared__ int s_off[PW_MAX_EXPERTS + 1];
+    __shared__ int s_run[PW_MAX_EXPERTS];
+    __shared__ int s_wc[NW * PW_MAX_EXPERTS];
+    __shared__ int s_tmp[NW];
 
+    // ---- fp32 logit and bound of expert e (one wave); column-permuted x and y = 0 for the token
     const uint16_t* xr = p.x + (size_t)t * d;
-    for (int c = tid * 8; c < d; c += kRouteThreads * 8) {
-        const uint4 v = *(const uint4*)(xr + c);
-        *(uint4*)(s_x + c) = v;
-        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int h = 0; h < 8; ++h) s_xf[c + h] = h2f((uint16_t)(vv[h >> 1] >> (16 * (h & 1))));
+    if (eb == 0) {
+        for (int c = tid; c < d; c += kRouteThreads) {
+            p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
+            p.y[(size_t)t * d + c] = 0.0f;
+        }
     }
-    for (int c = tid; c < d; c += kRouteThreads) {
-        p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
-        p.y[(size_t)t * d + c] = 0.0f;
+    const int e = eb * NW + wave;
+    if (e < E) {
+        float acc, sab;
+        approx_logit<NB>(p, t, e, lane, acc, sab);
+        if (lane == 0) {
+            const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
+            store_agent(p.ws.apx + (size_t)t * E + e, acc + bf);
+            store_agent(p.ws.bnd + (size_t)t * E + e, sab + fabsf(bf));
+        }
     }
-    if (tid == 0) s_ncand = 0;
+    vm_drain();
     __syncthreads();
+    if (tid == 0) s_last = __hip_atomic_fetch_add(p.ws.tok_cnt + t, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nb - 1);
+    __syncthreads();
+    if (!s_last) return;
 
-    // ---- fp32 logits and their error bound, one wave per expert
-    switch ((d + 511) >> 9) {
-        case 1: approx_logits<1>(p, s_xf, s_apx, s_bnd, wave, lane); break;
-        case 2: approx_logits<2>(p, s_xf, s_apx, s_bnd, wave, lane); break;
-        case 3: case 4: approx_logits<4>(p, s_xf, s_apx, s_bnd, wave, lane); break;
-        case 5: case 6: case 7: case 8: approx_logits<8>(p, s_xf, s_apx, s_bnd, wave, lane); break;
-        default: approx_logits<16>(p, s_xf, s_apx, s_bnd, wave, lane); break;
+    // ---- token t: candidates A_e >= a_k - 2*delta. Thread e ranks expert e among
+    // all (number of experts ahead of it in key order); rank k-1 holds a_k.
+    if (tid == 0) {
+        store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
+        s_ncand = 0;
+    }
+    for (int i = tid; i < E; i += kRouteThreads) {
+        s_apx[i] = load_agent(p.ws.apx + (size_t)t * E + i);
+        s_bnd[i] = load_agent(p.ws.bnd + (size_t)t * E + i);
     }
     __syncthreads();
-
-    // ---- candidates: A_e >= a_k - 2*delta. Thread e ranks expert e among all
-    // (number of experts ahead of it in key order); rank k-1 holds a_k.
     if (tid < E) {
         const float ve = s_apx[tid];
         int rank = 0;
@@ -251,14 +389,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     // ---- exact logits of the candidates, one wave per candidate
     const int nc = s_ncand;
     for (int ci = wave; ci < nc; ci += NW) {
-        const int e = s_cand[ci];
-        const uint16_t* wrow = p.wr + (size_t)e * d;
+        const int ec = s_cand[ci];
+        const uint16_t* wrow = p.wr + (size_t)ec * d;
         long long acc = 0;
         float sab = 0.0f;
         int bad = 0;
         for (int c = lane * 8; c < d; c += 512) {
             const uint4 wv = *(const uint4*)(wrow + c);
-            const uint4 xv = *(const uint4*)(s_x + c);
+            const uint4 xv = *(const uint4*)(xr + c);
             add_pair(xv.x, wv.x, acc, sab, bad);
             add_pair(xv.y, wv.y, acc, sab, bad);
             add_pair(xv.z, wv.z, acc, sab, bad);
@@ -272,7 +410,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
         }
         if (lane == 0) {
             if (p.bias) {
-                const float bf = h2f(p.bias[e]);
+                const float bf = h2f(p.bias[ec]);
                 bad |= !(fabsf(bf) < 32768.0f);
                 if (!bad) acc += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
                 sab += fabsf(bf);
@@ -287,12 +425,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     // ---- exact top-k: rank of each candidate among the candidates
     if (tid < nc) {
         const long long v = s_ex[tid];
-        const int e = s_cand[tid];
+        const int ec = s_cand[tid];
         int rank = 0;
-        for (int c2 = 0; c2 < nc; ++c2) rank += key_gt(s_ex[c2], s_cand[c2], v, e) ? 1 : 0;
+        for (int c2 = 0; c2 < nc; ++c2) rank += key_gt(s_ex[c2], s_cand[c2], v, ec) ? 1 : 0;
         if (rank < k) {
             s_selv[rank] = v;
-            s_sele[rank] = e;
+            s_sele[rank] = ec;
         }
     }
     __syncthreads();
@@ -307,141 +445,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
         }
         for (int j = 0; j < k; ++j) {
             const float wj = ex[j] / s;
-            p.ws.ids[(size_t)t * k + j] = s_sele[j];
-            p.ws.w[(size_t)t * k + j] = wj;
+            store_agent(p.ws.ids + (size_t)t * k + j, s_sele[j]);
+            store_agent(p.ws.w + (size_t)t * k + j, wj);
             if (p.o_ids) p.o_ids[(size_t)t * k + j] = s_sele[j];
             if (p.o_w) p.o_w[(size_t)t * k + j] = wj;
         }
+        vm_drain();
+        s_last = __hip_atomic_fetch_add(p.ws.route_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(p.T - 1);
+        if (s_last) store_agent(p.ws.route_done, 0u);   // every token has counted
     }
-}
+    __syncthreads();
+    if (!s_last) return;
 
-// ============================================================================ bucket sort + work lists
-
-// Exclusive scan over the 1024 threads of the bucket kernel; *total gets the sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(inc, off);
-        if (lane >= off) inc += o;
-    }
-    if (lane == 63) s_tmp[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        const int tv = lane < kBucketThreads / 64 ? s_tmp[lane] : 0;
-        int ti = tv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(ti, off);
-            if (lane >= off) ti += o;
-        }
-        if (lane < kBucketThreads / 64) s_tmp[32 + lane] = ti - tv;
-        if (lane == kBucketThreads / 64 - 1) s_tmp[64] = ti;
-    }
-    __syncthreads();
-    const int res = inc - v + s_tmp[32 + wave];
-    *total = s_tmp[64];
-    __syncthreads();
-    return res;
-}
-
-// One work-group: a stable counting sort of the T*k assignments by expert
-// (counts, exclusive offsets, assignments in ascending (t, j) per expert), and
-// the per-expert item prefix of each gemm work list.
-__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(BucketParams p) {
-    constexpr int NW = kBucketThreads / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = p.E, n = p.T * p.k;
-    __shared__ int s_cnt[PW_MAX_EXPERTS];
-    __shared__ int s_off[PW_MAX_EXPERTS + 1];
-    __shared__ int s_run[PW_MAX_EXPERTS];
-    __shared__ int s_wc[NW * PW_MAX_EXPERTS];
-    __shared__ int s_tmp[80];
-
-    const bool one_chunk = n <= kBucketThreads;
-    const int my_e = (one_chunk && tid < n) ? p.ws.ids[tid] : 0;
-    for (int e = tid; e < E; e += kBucketThreads) s_cnt[e] = 0;
-    __syncthreads();
-    if (one_chunk) {
-        if (tid < n) atomicAdd(&s_cnt[my_e], 1);
-    } else {
-        for (int i = tid; i < n; i += kBucketThreads) atomicAdd(&s_cnt[p.ws.ids[i]], 1);
-    }
-    __syncthreads();
-    {
-        int tot;
-        const int v = tid < E ? s_cnt[tid] : 0;
-        const int ex = block_excl_scan(v, s_tmp, &tot);
-        if (tid < E) s_off[tid] = ex;
-        if (tid == 0) s_off[E] = tot;
-    }
-    __syncthreads();
-    for (int e = tid; e <= E; e += kBucketThreads) {
-        p.ws.offsets[e] = s_off[e];
-        if (p.o_offsets) p.o_offsets[e] = s_off[e];
-        if (e < E) {
-            p.ws.counts[e] = s_cnt[e];
-            if (p.o_counts) p.o_counts[e] = s_cnt[e];
-            s_run[e] = s_off[e];
-        }
-    }
-    __syncthreads();
-    for (int base = 0; base < n; base += kBucketThreads) {
-        for (int j = tid; j < NW * E; j += kBucketThreads) s_wc[j] = 0;
-        __syncthreads();
-        const int i = base + tid;
-        const bool valid = i < n;
-        const int e = valid ? (one_chunk ? my_e : p.ws.ids[i]) : 0;
-        unsigned long long same = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const unsigned long long bb = __ballot(valid && ((e >> bit) & 1));
-            same &= ((e >> bit) & 1) ? bb : ~bb;
-        }
-        const int rank = __popcll(same & __lanemask_lt());
-        if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kBucketThreads) {
-            int run = s_run[ee];
-            for (int w = 0; w < NW; ++w) {
-                const int c = s_wc[w * E + ee];
-                s_wc[w * E + ee] = run;
-                run += c;
-            }
-            s_run[ee] = run;
-        }
-        __syncthreads();
-        if (valid) {
-            const int pos = s_wc[wave * E + e] + rank;
-            p.ws.sorted[pos] = i;
-            p.ws.slot_tok[pos] = i / p.k;   // token of the slot, and its routing weight
-            p.ws.slot_w[pos] = p.ws.w[i];
-            if (p.o_sorted) p.o_sorted[pos] = i;
-        }
-        __syncthreads();
-    }
-
-    // ---- work lists: list position 0 is the shared expert (long items first)
-    const int npos = E + p.has_shared;
-    int cnt = 0, tgu = 0, pdn = 1;
-    if (tid < npos) {
-        const bool sh = p.has_shared && tid == 0;
-        const int ex = sh ? E : tid - p.has_shared;
-        cnt = sh ? p.T : s_cnt[ex];
-        tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
-        pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
-    }
-    const int small = (cnt >= 1 && cnt <= kSmallTokens) ? 1 : 0;
-    const int groups = cnt > kSmallTokens ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
-    const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn, groups * p.tiles_dn * pdn};
-    const int stride = E + 2;
-    for (int l = 0; l < N_LISTS; ++l) {
-        int tot;
-        const int ex = block_excl_scan(tid < npos ? nitems[l] : 0, s_tmp, &tot);
-        if (tid < npos) p.ws.prefix[l * stride + tid] = ex;
-        if (tid == 0) p.ws.prefix[l * stride + npos] = tot;
-    }
+    // ---- the last token: bucket sort and work lists for the expert kernel
+    bucket_sort(p, s_cnt, s_off, s_run, s_wc, s_tmp);
 }
 
 // ============================================================================ dequant core
@@ -565,10 +583,6 @@ __device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* ti
         stripe[idx * 64 + row] = h | (h << 16);
     }
 }
-
-// Waits until every vector-memory operation this wave issued has completed
-// (s_waitcnt vmcnt(0); gfx9 encoding, other counters left at their maximum).
-__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int dw) {
     return dw == 0 ? q.x : dw == 1 ? q.y : dw == 2 ? q.z : q.w;
@@ -1048,9 +1062,9 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
     if (i < n) out[i] = f2h(h2f(x[i]) + y[i]);
 }
 
-__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_dep) {
+__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_counters) {
     if (threadIdx.x == 0) *ws.status = 0u;
-    for (int i = threadIdx.x; i < n_dep; i += 64) ws.dep[i] = 0u;
+    for (int i = threadIdx.x; i < n_counters; i += 64) ws.dep[i] = 0u;   // dep, tok_cnt, route_done
 }
 
 struct DebugParams {
@@ -1122,18 +1136,21 @@ int expert_lds_bytes(int tile_tokens) {
     return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + 2 * kPreWords * 4 + 16;
 }
 
-hipError_t launch_init_ws(const Workspace& ws, int n_dep, hipStream_t s) {
-    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws, n_dep);
+hipError_t launch_init_ws(const Workspace& ws, int n_counters, hipStream_t s) {
+    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws, n_counters);
     return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(route_kernel, dim3(p.T), dim3(kRouteThreads), 0, s, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_bucket(const BucketParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, s, p);
+    const int nb = (p.E + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+    const dim3 grid((unsigned)(p.T * nb));
+    switch ((p.d + 511) >> 9) {
+        case 1: hipLaunchKernelGGL(route_kernel<1>, grid, dim3(kRouteThreads), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(route_kernel<2>, grid, dim3(kRouteThreads), 0, s, p); break;
+        case 3: case 4: hipLaunchKernelGGL(route_kernel<4>, grid, dim3(kRouteThreads), 0, s, p); break;
+        case 5: case 6: case 7: case 8: hipLaunchKernelGGL(route_kernel<8>, grid, dim3(kRouteThreads), 0, s, p); break;
+        default: hipLaunchKernelGGL(route_kernel<16>, grid, dim3(kRouteThreads), 0, s, p); break;
+    }
     return hipGetLastError();
 }
 
