@@ -853,9 +853,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
         }
         __syncthreads();
         int par = 0;
+        // The two work-groups sharing a CU (w and w + G/2 in dispatch order)
+        // compete for its SIMDs, and at equal priority the older waves win, so
+        // the later work-group runs its items ~25 % slower. Their wave
+        // priorities swap every item so that both progress at the same rate.
+        const int slot = blockIdx.x >= gridDim.x / 2 ? 1 : 0;
+        int round = 0;
 
         while (true) {
             asm volatile("" : "+v"(tid), "+v"(r), "+v"(kg));
+            if (((round++ ^ slot) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
             const int nch = n_chunks(it);
             const int ntl = (it.nl + 15) >> 4;
             const int* tb = s_tok + par * kTokWords;
@@ -875,10 +883,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             const bool has_next = next < n_items;
             Item nit = it;
             TokInfo ntk{0, 0, 0.0f};
-            if (has_next) {
-                nit = decode(next);
-                ntk = tokinfo(nit);
-            }
+            if (has_next) nit = decode(next);
 
             uint32_t boff[NT];
             bool bok[NT];
@@ -951,6 +956,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 if (has_next) {
                     load_chunk(nit, 0, pa0, pa1);
                     lut_load(nit, st);
+                    ntk = tokinfo(nit);   // its scalar loads are waited together with the chunk's
                 }
                 fetched = true;
             };
@@ -986,7 +992,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 }
             }
             __syncthreads();   // every wave is done with the LUT stripe; partial sums visible
-            if (has_next) publish_item(nit, st, ntk, par ^ 1);
 
             // sum of the two half-line partials of registers 2*kh, 2*kh+1 and the epilogue
 #pragma unroll
@@ -1027,6 +1032,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     }
                 }
             }
+            // the next item's LUT rows and token rows (written while the act stores drain)
+            if (has_next) publish_item(nit, st, ntk, par ^ 1);
             if (it.mode == 0) vm_drain();   // this wave's act stores are complete
             __syncthreads();   // next item's LUT rows and token rows are in place; partials read
             if (it.mode == 0 && tid == 0)
