@@ -146,7 +146,6 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_stk = off;    off += al(sizeof(int32_t) * (size_t)T * k);
     const size_t o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
     const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
-    const size_t o_xp = off;     off += al(sizeof(uint16_t) * (size_t)T * d);
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
     const size_t o_st = off;     off += al(sizeof(uint32_t));
     const size_t o_apx = off;    off += al(sizeof(float) * (size_t)T * E);
@@ -179,7 +178,6 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.slot_tok = (int32_t*)(b + o_stk);
     L->ws.slot_w = (float*)(b + o_sw);
     L->ws.prefix = (int32_t*)(b + o_pre);
-    L->ws.xperm = (uint16_t*)(b + o_xp);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
     L->ws.apx = (float*)(b + o_apx);
@@ -436,7 +434,8 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     L->gp_gu.tiles_r = D.d_ffn / 32;
     L->gp_gu.tiles_s = D.d_ffn_shared / 32;
     L->gp_gu.pieces_r = L->gp_gu.pieces_s = 1;
-    L->gp_gu.b_bytes = (uint32_t)((size_t)D.max_tokens * d * 2);
+    L->gp_gu.x = (const uint16_t*)x;
+    L->gp_gu.b_bytes = (uint32_t)((size_t)T * d * 2);
     // down + weighted scatter-accumulate: items of 64 rows of d
     L->gp_dn = gp;
     L->gp_dn.tiles_r = d / 64;

@@ -33,7 +33,6 @@ struct Workspace {
     int32_t* slot_tok;   // [max_T*k]    token t of each sorted slot
     float* slot_w;       // [max_T*k]    routing weight of each sorted slot
     int32_t* prefix;     // [N_LISTS][E+2]
-    uint16_t* xperm;     // [max_T][d]   x with columns permuted inside 32-groups
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
     float* apx;          // [max_T][E]   fp32 router logits (route kernel, between work-groups)
@@ -68,7 +67,7 @@ struct RouteParams {
 // of the work-group owns rows 16*(w >> 1) .. +15 and half-line w & 1 of every
 // 128-byte plane line.
 // gate_up: set 0 = gate rows [f0, f0+32), set 1 = up rows [f0, f0+32), K = d,
-//          B = xperm rows (tokens), epilogue SwiGLU -> act (fp16).
+//          B = x rows (tokens), epilogue SwiGLU -> act (fp16).
 // down:    set 0 = rows [r0, r0+32), set 1 = rows [r0+32, r0+64), K = F (in
 //          pieces of kDownPiece columns), B = act rows (slots), epilogue
 //          w * o atomically added to y (fp32).
@@ -83,7 +82,8 @@ struct GemmParams {
     Workspace ws;
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
-    uint32_t b_bytes;         // size of the B-operand buffer (xperm or act)
+    const uint16_t* x;        // layer input (gate_up B operand)
+    uint32_t b_bytes;         // size of the B-operand buffer (x or act)
     float* y;
 };
 

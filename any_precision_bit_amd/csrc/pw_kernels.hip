@@ -33,8 +33,8 @@
 // 16-bit LDS read fetches the fp16 weight from the LUT stripe (dword idx*64 +
 // slot holds the two row-sets' entries of one row, low/high half; two copies
 // so each half-wave hits 32 distinct banks). Eight looked-up weights form one
-// MFMA A operand; the B operand (activations) is stored with the same in-group
-// column permutation, so the contraction is unchanged.
+// MFMA A operand: step m of a 32-column group takes columns 8m..8m+7, so the B
+// operand is the activation row as stored.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -87,14 +87,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(4))) T* kconst(const T* p) {
     return (const __attribute__((address_space(4))) T*)(size_t)p;
-}
-
-// Position of column c (0..31) of a 32-column group in the permuted activation
-// layout: column 8k + i goes to 8*(i>>1) + 2k + (i&1). Eight consecutive
-// permuted positions 8m..8m+7 are the columns one MFMA step m consumes.
-__device__ __forceinline__ int perm32(int c) {
-    const int k = c >> 3, i = c & 7;
-    return 8 * (i >> 1) + 2 * k + (i & 1);
 }
 
 // ============================================================================ route
@@ -332,13 +324,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __shared__ int s_wc[NW * PW_MAX_EXPERTS];
     __shared__ int s_tmp[NW];
 
-    // ---- fp32 logit and bound of expert e (one wave); column-permuted x and y = 0 for the token
+    // ---- fp32 logit and bound of expert e (one wave); y = 0 for the token
     const uint16_t* xr = p.x + (size_t)t * d;
     if (eb == 0) {
-        for (int c = tid; c < d; c += kRouteThreads) {
-            p.ws.xperm[(size_t)t * d + (c & ~31) + perm32(c & 31)] = xr[c];
-            p.y[(size_t)t * d + c] = 0.0f;
-        }
+        for (int c = tid; c < d; c += kRouteThreads) p.y[(size_t)t * d + c] = 0.0f;
     }
     const int e = eb * NW + wave;
     if (e < E) {
@@ -496,20 +485,18 @@ __device__ __forceinline__ void slots_to_indices(const uint32_t (&sl)[8], uint32
 }
 
 // A fragment of MFMA step m from the index words of one 32-column group:
-// half 2k+e = LUT[index of column 8k + 2m + e]. `slot` is the lane's LDS address
-// of stripe entry 0 (segment base + row slot * 4); byte 1 of it is replaced by
-// the index, i.e. entry idx sits idx*256 bytes further. hoff selects the row-set
-// (0: low half, 2: high half of the stripe dword).
+// half j = LUT[index of column 8m + j], so step m consumes eight consecutive
+// columns and the B operand is the activation row as stored. Column 8m + j is
+// byte m of index word j. `slot` is the lane's LDS address of stripe entry 0
+// (segment base + row slot * 4); byte 1 of it is replaced by the index, i.e.
+// entry idx sits idx*256 bytes further. hoff selects the row-set (0: low half,
+// 2: high half of the stripe dword).
 __device__ __forceinline__ half8 lut_fragment(const uint32_t (&rw)[8], int m, uint32_t slot, int hoff) {
     half8 a;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const uint32_t addr =
-                __builtin_amdgcn_perm(rw[2 * m + e], slot, 0x03020400u | (uint32_t)(kk << 8));
-            a[2 * kk + e] = *(lds_half*)(size_t)(addr + hoff);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t addr = __builtin_amdgcn_perm(rw[j], slot, 0x03020400u | (uint32_t)(m << 8));
+        a[j] = *(lds_half*)(size_t)(addr + hoff);
     }
     return a;
 }
@@ -619,7 +606,7 @@ __device__ __forceinline__ TokInfo fetch_tokinfo(const GemmParams& p, const Item
         const int slot = sh ? (p.shared_base + tkn) : (base + tkn);
         const int tok = sh ? tkn : p.ws.slot_tok[slot];
         if (MODE == 0) {
-            tk.brow = tok;    // xperm row
+            tk.brow = tok;    // x row
             tk.orow = slot;   // act row
         } else {
             tk.brow = slot;   // act row
@@ -867,10 +854,10 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             const int nch = n_chunks(it);
             const int ntl = (it.nl + 15) >> 4;
             const int* tb = s_tok + par * kTokWords;
-            // B operand: xperm rows (gate_up) or act rows (down)
+            // B operand: x rows (gate_up) or act rows (down)
             const int ldb = it.mode == 0 ? g.d : g.ld_act;
             const __amdgpu_buffer_rsrc_t brsrc =
-                it.mode == 0 ? make_rsrc(g.ws.xperm, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
+                it.mode == 0 ? make_rsrc(g.x, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
             if (it.mode == 1) {
                 // every gate_up item of this expert's K-piece has released its act rows
                 const uint32_t need = (uint32_t)((it.klen >> 5) * ((it.n_tok + 16 * NT - 1) / (16 * NT)));
@@ -1016,12 +1003,12 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     if (it.mode == 0) {
                         const float a0 = g0 / (1.0f + expf(-g0)) * u0;
                         const float a1 = g1 / (1.0f + expf(-g1)) * u1;
-                        const int f = it.rows0 + row;   // even: f, f+1 are adjacent permuted columns
+                        const int f = it.rows0 + row;   // even: f, f+1 are adjacent act columns
                         const uint32_t pk = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
                         // device-coherent store: written through to the memory side, so a down
                         // item on another XCD that reads the row after the counter sees it
-                        __hip_atomic_store((uint32_t*)(g.ws.act + (size_t)orow * g.ld_act + (f & ~31) + perm32(f & 31)),
-                                           pk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store((uint32_t*)(g.ws.act + (size_t)orow * g.ld_act + f), pk,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     } else {
                         const float wv = __int_as_float(tb[128 + tok_i]);
                         float* yr = g.y + (size_t)orow * g.d;
@@ -1125,11 +1112,8 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
                 for (int m = 0; m < 4; ++m) {
                     const half8 a = lut_fragment(rw, m, slot, 0);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            p.w_out[rowoff + cg + 8 * kk + 2 * m + e] =
-                                __builtin_bit_cast(uint16_t, (_Float16)a[2 * kk + e]);
+                    for (int j = 0; j < 8; ++j)
+                        p.w_out[rowoff + cg + 8 * m + j] = __builtin_bit_cast(uint16_t, (_Float16)a[j]);
                 }
             }
         }
