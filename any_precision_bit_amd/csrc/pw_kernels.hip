@@ -904,13 +904,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             // arrive while the transposes and lookups run. Lanes past K hold zero B
             // fragments, so their A fragments need no masking. A wave whose half of
             // the chunk lies wholly past K skips it.
+            // bfr: B fragments of the current dword. Those of dword 0 of a chunk are
+            // loaded before the plane prefetch issued at the chunk boundary: loads
+            // complete in issue order, so a fragment loaded after a prefetch is
+            // waited on only together with it.
+            half8 bfr[NT][4];
             auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
                 if (ch * 1024 + kh * 512 >= it.klen) return;
                 const bool vg = lane_col(ch) < it.klen;
-                half8 bfr[NT][4];
 #pragma unroll
                 for (int dw = 0; dw < 4; ++dw) {
-                    load_b(ch, dw, bfr, vg);
+                    if (dw > 0) load_b(ch, dw, bfr, vg);
                     uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -947,14 +951,20 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 }
                 fetched = true;
             };
+            auto first_b = [&](int ch) {
+                if (ch < nch) load_b(ch, 0, bfr, lane_col(ch) < it.klen);
+            };
+            first_b(0);
             if (1 < nch) load_chunk(it, 1, pb0, pb1);
 #pragma unroll 1
             for (int ch = 0; ch < nch; ch += 2) {
                 compute_chunk(ch, pa0, pa1);
+                first_b(ch + 1);
                 if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
                 else if (ch + 1 < nch) fetch_next();
                 if (ch + 1 >= nch) break;
                 compute_chunk(ch + 1, pb0, pb1);
+                first_b(ch + 2);
                 if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
             }
             if (!fetched) fetch_next();
