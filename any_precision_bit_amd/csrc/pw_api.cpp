@@ -148,8 +148,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
     const size_t o_st = off;     off += al(sizeof(uint32_t));
-    const size_t o_apx = off;    off += al(sizeof(float) * (size_t)T * E);
-    const size_t o_bnd = off;    off += al(sizeof(float) * (size_t)T * E);
+    const size_t o_lg = off;     off += al(sizeof(long long) * (size_t)T * E);
     const int dep_stride = (L->f_max + pw::kDownPiece - 1) / pw::kDownPiece;
     const int n_dep = (E + 1) * dep_stride + 1;
     const int n_counters = n_dep + T + 1;   // dep, tok_cnt, route_done
@@ -180,8 +179,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.prefix = (int32_t*)(b + o_pre);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
-    L->ws.apx = (float*)(b + o_apx);
-    L->ws.bnd = (float*)(b + o_bnd);
+    L->ws.lg = (long long*)(b + o_lg);
     L->ws.dep = (uint32_t*)(b + o_dep);
     L->ws.tok_cnt = L->ws.dep + n_dep;
     L->ws.route_done = L->ws.tok_cnt + T;

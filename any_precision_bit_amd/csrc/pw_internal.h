@@ -35,8 +35,7 @@ struct Workspace {
     int32_t* prefix;     // [N_LISTS][E+2]
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
-    float* apx;          // [max_T][E]   fp32 router logits (route kernel, between work-groups)
-    float* bnd;          // [max_T][E]   their sum |x w| bounds
+    long long* lg;       // [max_T][E]   exact router logits, units of 2^-48 (route kernel, between work-groups)
     // counters, contiguous and zeroed once; every launch leaves them at zero
     uint32_t* dep;       // [(E+1)*dep_stride + 1]  gate_up items done per (list position, down
                          //              K-piece); last word: work-groups finished (expert kernel)
@@ -111,7 +110,8 @@ int expert_lds_bytes(int tile_tokens);
 constexpr int kSmallTokens = 16;          // experts with 1..16 tokens: one 16-token MFMA tile
 constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
-constexpr int kRouteThreads = 256;          // route kernel: 4 waves, one expert each
+constexpr int kRouteThreads = 256;          // route kernel: 4 waves
+constexpr int kRouteExpertsPerWave = 2;     // router rows per wave
 constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)
 
 }  // namespace pw

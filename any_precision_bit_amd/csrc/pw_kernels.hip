@@ -6,15 +6,12 @@
 // and fuses routing, SwiGLU expert activation and weighted accumulation.
 //
 // Kernels, in stream order per forward:
-//   route_kernel   T * ceil(E/4) work-groups, one expert per wave: fp32 router
-//                  logits with an error bound; per token, the last work-group
-//                  recomputes the candidates the bound cannot rule out exactly
-//                  (int64, units of 2^-48) and takes the exact top-k and the
-//                  softmax over the k selected; the last token's work-group
-//                  sorts the assignments by expert (counts, offsets, stable
-//                  order, each slot's token and weight) and writes the
-//                  per-expert work-item prefixes. Also the column-permuted copy
-//                  of x, and y = 0.
+//   route_kernel   T * ceil(E/8) work-groups, two experts per wave: exact router
+//                  logits (int64, units of 2^-48); per token, the last work-group
+//                  takes the exact top-k and the softmax over the k selected; the
+//                  last token's work-group sorts the assignments by expert
+//                  (counts, offsets, stable order, each slot's token and weight)
+//                  and writes the per-expert work-item prefixes. Also y = 0.
 //   expert_kernel  persistent, one launch per token-tile size: gate and up of
 //                  (expert, 32-row tile, token group) items (bit-plane unpack +
 //                  LUT dequant into MFMA A fragments, MFMA 16x16x32 fp16 with
@@ -115,44 +112,6 @@ __device__ __forceinline__ void add_pair(uint32_t xw, uint32_t ww, long long& ac
 template <typename V>
 __device__ __forceinline__ bool key_gt(V va, int ea, V vb, int eb) {
     return va > vb || (va == vb && ea < eb);
-}
-
-// fp32 logit and bound of expert e for token t, one wave: lane l takes columns
-// l*8 + 512*i; products of two fp16 values are exact in fp32.
-template <int NB>
-__device__ __forceinline__ void approx_logit(const RouteParams& p, int t, int e, int lane, float& acc_out,
-                                             float& sab_out) {
-    const int d = p.d;
-    const uint16_t* xr = p.x + (size_t)t * d;
-    const uint16_t* wr = p.wr + (size_t)e * d;
-    uint4 xv[NB], wv[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int c = lane * 8 + 512 * i;
-        const bool ok = c < d;
-        xv[i] = ok ? *(const uint4*)(xr + c) : make_uint4(0, 0, 0, 0);
-        wv[i] = ok ? *(const uint4*)(wr + c) : make_uint4(0, 0, 0, 0);
-    }
-    float acc = 0.0f, sab = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const uint32_t xa[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-        const uint32_t wa[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-#pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            const float xf = h2f((uint16_t)(xa[h >> 1] >> (16 * (h & 1))));
-            const float wf = h2f((uint16_t)(wa[h >> 1] >> (16 * (h & 1))));
-            acc = fmaf(xf, wf, acc);
-            sab = fmaf(fabsf(xf), fabsf(wf), sab);
-        }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        acc += __shfl_xor(acc, off);
-        sab += __shfl_xor(sab, off);
-    }
-    acc_out = acc;
-    sab_out = sab;
 }
 
 // Exclusive scan over the kRouteThreads threads; *total gets the sum.
@@ -290,32 +249,75 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     }
 }
 
-// Routing in one launch of T * ceil(E/4) work-groups of 4 waves; work-group
-// (t, eb) computes, one expert per wave, the fp32 logits of experts 4*eb .. +3
-// for token t with an error bound. Selection is exact although the bulk of
-// the logits is fp32: every fp32 logit A_e is within delta of the exact value
-// L_e, so any expert of the exact top-k has A_e >= a_k - 2*delta, a_k being the
-// k-th largest A. The work-group that finishes token t last (a counter per
-// token) recomputes only those candidates exactly (int64, units of 2^-48),
-// takes the top-k over the exact values and the softmax over the k; the one
-// that finishes the last token does the bucket sort and the work lists.
-// Values passed between work-groups are device-coherent stores, drained before
-// the counter increment that publishes them, and device-coherent loads.
-template <int NB>
+// Exact router logits of kRouteExpertsPerWave experts e0, e0 + 1, ... for token
+// t, one wave (lane l takes columns l*8 + 512*i, four 512-column blocks per
+// batch, all loads of a batch issued first): int64 sums in units of 2^-48,
+// with sum |x w| and the out-of-range flag of each.
+__device__ __forceinline__ void exact_logits(const RouteParams& p, int t, int e0, int lane,
+                                             long long (&acc)[kRouteExpertsPerWave],
+                                             float (&sab)[kRouteExpertsPerWave], int (&bad)[kRouteExpertsPerWave]) {
+    constexpr int EW = kRouteExpertsPerWave;
+    const int d = p.d;
+    const uint16_t* xr = p.x + (size_t)t * d;
+#pragma unroll
+    for (int j = 0; j < EW; ++j) {
+        acc[j] = 0;
+        sab[j] = 0.0f;
+        bad[j] = 0;
+    }
+    for (int c0 = 0; c0 < d; c0 += 2048) {
+        uint4 xv[4], wv[EW][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + lane * 8 + 512 * i;
+            const bool ok = c < d;
+            xv[i] = ok ? *(const uint4*)(xr + c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < EW; ++j) {
+                const bool okj = ok && e0 + j < p.E;
+                wv[j][i] = okj ? *(const uint4*)(p.wr + (size_t)(e0 + j) * d + c) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < EW; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                add_pair(xv[i].x, wv[j][i].x, acc[j], sab[j], bad[j]);
+                add_pair(xv[i].y, wv[j][i].y, acc[j], sab[j], bad[j]);
+                add_pair(xv[i].z, wv[j][i].z, acc[j], sab[j], bad[j]);
+                add_pair(xv[i].w, wv[j][i].w, acc[j], sab[j], bad[j]);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < EW; ++j) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            acc[j] += __shfl_xor(acc[j], off);
+            sab[j] += __shfl_xor(sab[j], off);
+            bad[j] |= __shfl_xor(bad[j], off);
+        }
+    }
+}
+
+// Routing and bucket sort in one launch of T * ceil(E / (4 * kRouteExpertsPerWave))
+// work-groups of 4 waves. Work-group (t, eb) computes the exact logits (int64,
+// units of 2^-48) of its experts for token t, kRouteExpertsPerWave per wave:
+// with |x|, |w| < 128, x*2^24 and w*2^24 are integers below 2^31 and their
+// products are exact. The work-group that finishes token t last (a counter per
+// token) ranks all E exact logits (ties to the lower expert index), keeps the
+// top k and takes the softmax over them; the one that finishes the last token
+// does the bucket sort and the work lists. Values passed between work-groups
+// are device-coherent stores, drained before the counter increment that
+// publishes them, and device-coherent loads.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
-    constexpr int NW = kRouteThreads / 64;
+    constexpr int NW = kRouteThreads / 64, EW = kRouteExpertsPerWave;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
-    const int nb = (E + NW - 1) / NW;
+    const int nb = (E + NW * EW - 1) / (NW * EW);
     const int t = blockIdx.x / nb, eb = blockIdx.x - t * nb;
-    __shared__ float s_apx[PW_MAX_EXPERTS];
-    __shared__ float s_bnd[PW_MAX_EXPERTS];
-    __shared__ int s_cand[PW_MAX_EXPERTS];
     __shared__ long long s_ex[PW_MAX_EXPERTS];
     __shared__ long long s_selv[PW_MAX_TOP_K];
     __shared__ int s_sele[PW_MAX_TOP_K];
-    __shared__ float s_tau;
-    __shared__ int s_ncand;
     __shared__ int s_last;
     // bucket sort (last work-group only)
     __shared__ int s_cnt[PW_MAX_EXPERTS];
@@ -324,19 +326,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __shared__ int s_wc[NW * PW_MAX_EXPERTS];
     __shared__ int s_tmp[NW];
 
-    // ---- fp32 logit and bound of expert e (one wave); y = 0 for the token
-    const uint16_t* xr = p.x + (size_t)t * d;
+    // ---- exact logits of this work-group's experts; y = 0 for the token
     if (eb == 0) {
         for (int c = tid; c < d; c += kRouteThreads) p.y[(size_t)t * d + c] = 0.0f;
     }
-    const int e = eb * NW + wave;
-    if (e < E) {
-        float acc, sab;
-        approx_logit<NB>(p, t, e, lane, acc, sab);
+    const int e0 = (eb * NW + wave) * EW;
+    if (e0 < E) {
+        long long acc[EW];
+        float sab[EW];
+        int bad[EW];
+        exact_logits(p, t, e0, lane, acc, sab, bad);
         if (lane == 0) {
-            const float bf = p.bias ? h2f(p.bias[e]) : 0.0f;
-            store_agent(p.ws.apx + (size_t)t * E + e, acc + bf);
-            store_agent(p.ws.bnd + (size_t)t * E + e, sab + fabsf(bf));
+#pragma unroll
+            for (int j = 0; j < EW; ++j) {
+                const int e = e0 + j;
+                if (e >= E) break;
+                if (p.bias) {
+                    const float bf = h2f(p.bias[e]);
+                    bad[j] |= !(fabsf(bf) < 32768.0f);
+                    if (!bad[j]) acc[j] += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
+                    sab[j] += fabsf(bf);
+                }
+                // sum |x w| < 2^15 keeps every partial sum inside int64 (fp32 bound, wide margin)
+                if (bad[j] || !(sab[j] < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
+                store_agent(p.ws.lg + (size_t)t * E + e, acc[j]);
+            }
         }
     }
     vm_drain();
@@ -346,80 +360,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __syncthreads();
     if (!s_last) return;
 
-    // ---- token t: candidates A_e >= a_k - 2*delta. Thread e ranks expert e among
-    // all (number of experts ahead of it in key order); rank k-1 holds a_k.
-    if (tid == 0) {
-        store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
-        s_ncand = 0;
-    }
-    for (int i = tid; i < E; i += kRouteThreads) {
-        s_apx[i] = load_agent(p.ws.apx + (size_t)t * E + i);
-        s_bnd[i] = load_agent(p.ws.bnd + (size_t)t * E + i);
-    }
+    // ---- token t: exact top-k by rank (number of experts ahead in key order)
+    if (tid == 0) store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
+    for (int i = tid; i < E; i += kRouteThreads) s_ex[i] = load_agent(p.ws.lg + (size_t)t * E + i);
     __syncthreads();
     if (tid < E) {
-        const float ve = s_apx[tid];
-        int rank = 0;
-        float bm = 0.0f;
-        for (int e2 = 0; e2 < E; ++e2) {
-            rank += key_gt(s_apx[e2], e2, ve, tid) ? 1 : 0;
-            bm = fmaxf(bm, s_bnd[e2]);
-        }
-        if (rank == k - 1) {
-            // |A_e - L_e| <= gamma_(d+1) * sum|x w| + |bias|-rounding: (d+2) * 2^-24 covers both
-            const float delta = bm * (float)(d + 2) * 5.9604645e-8f * 1.001f + 1e-30f;
-            s_tau = ve - 2.0f * delta - fabsf(ve) * 2.4e-7f - 2.0f * delta * 2.4e-7f;
-        }
-    }
-    __syncthreads();
-    if (tid < E && s_apx[tid] >= s_tau) s_cand[atomicAdd(&s_ncand, 1)] = tid;
-    __syncthreads();
-
-    // ---- exact logits of the candidates, one wave per candidate
-    const int nc = s_ncand;
-    for (int ci = wave; ci < nc; ci += NW) {
-        const int ec = s_cand[ci];
-        const uint16_t* wrow = p.wr + (size_t)ec * d;
-        long long acc = 0;
-        float sab = 0.0f;
-        int bad = 0;
-        for (int c = lane * 8; c < d; c += 512) {
-            const uint4 wv = *(const uint4*)(wrow + c);
-            const uint4 xv = *(const uint4*)(xr + c);
-            add_pair(xv.x, wv.x, acc, sab, bad);
-            add_pair(xv.y, wv.y, acc, sab, bad);
-            add_pair(xv.z, wv.z, acc, sab, bad);
-            add_pair(xv.w, wv.w, acc, sab, bad);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            acc += __shfl_xor(acc, off);
-            sab += __shfl_xor(sab, off);
-            bad |= __shfl_xor(bad, off);
-        }
-        if (lane == 0) {
-            if (p.bias) {
-                const float bf = h2f(p.bias[ec]);
-                bad |= !(fabsf(bf) < 32768.0f);
-                if (!bad) acc += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
-                sab += fabsf(bf);
-            }
-            // sum |x w| < 2^15 keeps every partial sum inside int64 (fp32 bound, wide margin)
-            if (bad || !(sab < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
-            s_ex[ci] = acc;
-        }
-    }
-    __syncthreads();
-
-    // ---- exact top-k: rank of each candidate among the candidates
-    if (tid < nc) {
         const long long v = s_ex[tid];
-        const int ec = s_cand[tid];
         int rank = 0;
-        for (int c2 = 0; c2 < nc; ++c2) rank += key_gt(s_ex[c2], s_cand[c2], v, ec) ? 1 : 0;
+        for (int e2 = 0; e2 < E; ++e2) rank += key_gt(s_ex[e2], e2, v, tid) ? 1 : 0;
         if (rank < k) {
             s_selv[rank] = v;
-            s_sele[rank] = ec;
+            s_sele[rank] = tid;
         }
     }
     __syncthreads();
@@ -1143,15 +1094,9 @@ hipError_t launch_init_ws(const Workspace& ws, int n_counters, hipStream_t s) {
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-    const int nb = (p.E + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
-    const dim3 grid((unsigned)(p.T * nb));
-    switch ((p.d + 511) >> 9) {
-        case 1: hipLaunchKernelGGL(route_kernel<1>, grid, dim3(kRouteThreads), 0, s, p); break;
-        case 2: hipLaunchKernelGGL(route_kernel<2>, grid, dim3(kRouteThreads), 0, s, p); break;
-        case 3: case 4: hipLaunchKernelGGL(route_kernel<4>, grid, dim3(kRouteThreads), 0, s, p); break;
-        case 5: case 6: case 7: case 8: hipLaunchKernelGGL(route_kernel<8>, grid, dim3(kRouteThreads), 0, s, p); break;
-        default: hipLaunchKernelGGL(route_kernel<16>, grid, dim3(kRouteThreads), 0, s, p); break;
-    }
+    constexpr int per_wg = (kRouteThreads / 64) * kRouteExpertsPerWave;
+    const int nb = (p.E + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL(route_kernel, dim3((unsigned)(p.T * nb)), dim3(kRouteThreads), 0, s, p);
     return hipGetLastError();
 }
 
