@@ -8,7 +8,9 @@ accumulation) of one layer over the batch. Steps rotate over byte-identical
 clones of the pages at distinct addresses so that the working set exceeds the
 on-chip caches and the weights stream from HBM.
 
-Prints one JSON line on stdout; diagnostics go to stderr.
+Prints one JSON line on stdout; diagnostics go to stderr. With --sweep it
+instead times one layer forward of every workload shape (c0, c1, c2 at T=1 and
+T=64, c3, one c4 layer at T=256) and prints a markdown table.
 """
 from __future__ import annotations
 
@@ -55,6 +57,83 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
+# (label, config, tokens or None for the config's own, rotation clones); c0 is cache-resident
+SWEEP = [("c0", "c0", None, 1), ("c1", "c1", None, 8), ("c2 T=1", "c2", 1, 8), ("c2 T=64", "c2", 64, 4),
+         ("c3", "c3", None, 4), ("c4 layer 0, T=256, first plan", "c4", None, 4)]
+
+
+def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
+    """Per-call times of one layer forward (routing + experts) for every workload shape:
+    warm-up calls, then timed calls each bracketed by HIP events on the launch stream,
+    rotating over byte-identical page clones."""
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    for label, key, T, M in SWEEP:
+        cfg = synth.CONFIGS[key]
+        if T is not None:
+            cfg = cfg.with_tokens(T)
+        t0 = time.time()
+        x = f16(synth.tokens(cfg))
+        wr_h, bias_h = synth.router(cfg)
+        wr = f16(wr_h)
+        bias = f16(bias_h) if bias_h is not None else None
+        counts = None
+        if cfg.bits_rule == "frequency":
+            # the plan follows the batch's routing counts; ranked here in fp64 (input set-up only)
+            lg = x.double() @ wr.double().T + (bias.double() if bias is not None else 0.0)
+            ids = torch.topk(lg, cfg.k, dim=1).indices
+            counts = torch.bincount(ids.reshape(-1), minlength=cfg.E).cpu().numpy()
+        bits = synth.initial_bits(cfg, counts=counts)
+        blocks = synth.make_layer_blocks(cfg, bits)
+        base = {}
+        for (e, lin), blk in blocks.items():
+            b = int(bits[e, lin])
+            base[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes[:b])).to(dev),
+                              f16(lut_page(blk.luts[b])), b)
+        del blocks
+        lays = []
+        for c in range(M):
+            pages = base if c == 0 else {kk: (p.clone(), l.clone(), b) for kk, (p, l, b) in base.items()}
+            lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+            lay.plan_set(bits)
+            for (e, lin), (p, l, b) in pages.items():
+                lay.bind(e, lin, [p[i] for i in range(b)], l, b)
+            lays.append((lay, pages, torch.empty((cfg.T, cfg.d), device=dev)))
+        torch.cuda.synchronize()
+        log(f"{label}: pages ready in {time.time() - t0:.1f}s")
+        for i in range(args.warmup):
+            lay, _, y = lays[i % M]
+            lay.forward(x, wr, bias, y=y, stream=stream)
+        n = max(args.steps // 4, 50)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            lay, _, y = lays[i % M]
+            evs[i][0].record(stream)
+            lay.forward(x, wr, bias, y=y, stream=stream)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        nb = lays[0][0].last_bytes(stream)
+        layer_bytes = nb[0] + nb[1] + nb[2]
+        med = float(np.median(us))
+        rows.append((label, cfg.T, M, layer_bytes / 1e6, med, float(np.percentile(us, 10)),
+                     float(np.percentile(us, 90)), layer_bytes / (med * 1e-6) / 1e9, cfg.T / (med * 1e-6)))
+        log(f"{label}: median {med:.1f} us")
+        for lay, _, _ in lays:
+            lay.close()
+        del lays, base
+        torch.cuda.empty_cache()
+    print("| workload | T | clones | algorithmic MB | median us | p10 us | p90 us | GB/s | HBM % | tokens/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for label, T, M, mb, med, p10, p90, gbs, tps in rows:
+        print(f"| {label} | {T} | {M} | {mb:.1f} | {med:.1f} | {p10:.1f} | {p90:.1f} | {gbs:.0f} | "
+              f"{100 * gbs / HBM_PEAK_GBS:.1f} | {tps:,.0f} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +142,8 @@ def main():
     ap.add_argument("--clones", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload shape (per-call median, p10, p90) and print a table")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -87,6 +168,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration} MiB x 5 (reads and writes {n} bytes per copy)")
+        return
+    if args.sweep:
+        sweep(args, torch, synth, PagedMoELayer, lut_page, dev)
         return
     cfg = synth.CONFIGS["c1"]
     T = cfg.T
