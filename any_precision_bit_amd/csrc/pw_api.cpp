@@ -241,7 +241,7 @@ pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
             ep.dn.list = pw::LIST_DN_SMALL;
             if ((e = pw::launch_experts(pw::kSmallTokens, ep, L->n_cu, s)) != hipSuccess)
                 return hip_fail(e, "expert kernel");
-            if (T > pw::kSmallTokens) {
+            if (T > pw::kSmallMax) {
                 ep.gu.list = pw::LIST_GU_LARGE;
                 ep.dn.list = pw::LIST_DN_LARGE;
                 if ((e = pw::launch_experts(pw::kLargeTokens, ep, L->n_cu, s)) != hipSuccess)

@@ -107,7 +107,8 @@ hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int
 // LDS bytes of the expert kernel for items of tile_tokens tokens.
 int expert_lds_bytes(int tile_tokens);
 
-constexpr int kSmallTokens = 16;          // experts with 1..16 tokens: one 16-token MFMA tile
+constexpr int kSmallTokens = 16;          // token group of the one-tile kernel (one 16-token MFMA tile)
+constexpr int kSmallMax = 32;             // experts with 1..32 tokens: groups of 16 in the one-tile kernel
 constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
 constexpr int kRouteThreads = 256;          // route kernel: 4 waves

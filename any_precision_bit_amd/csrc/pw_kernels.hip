@@ -231,8 +231,11 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
             tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
             pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
         }
-        const int small = (cnt >= 1 && cnt <= kSmallTokens) ? 1 : 0;
-        const int groups = cnt > kSmallTokens ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
+        // up to kSmallMax tokens: 16-token groups in the one-tile kernel (at two
+        // work-groups per CU, two such items cost less CU time than one 64-token
+        // item at one work-group per CU); beyond: 64-token groups
+        const int small = (cnt >= 1 && cnt <= kSmallMax) ? (cnt + kSmallTokens - 1) / kSmallTokens : 0;
+        const int groups = cnt > kSmallMax ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
         const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn,
                                      groups * p.tiles_dn * pdn};
 #pragma unroll
