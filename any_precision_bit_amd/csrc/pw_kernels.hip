@@ -138,6 +138,43 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
     return inc - v + before;
 }
 
+// Exclusive scans of N values per thread at once (one pair of barriers for all);
+// s_tmp holds N * (kRouteThreads / 64) ints.
+template <int N>
+__device__ __forceinline__ void block_excl_scan_n(const int (&v)[N], int* s_tmp, int (&ex)[N], int (&total)[N]) {
+    constexpr int NW = kRouteThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc[N];
+#pragma unroll
+    for (int l = 0; l < N; ++l) inc[l] = v[l];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int l = 0; l < N; ++l) {
+            const int o = __shfl_up(inc[l], off);
+            if (lane >= off) inc[l] += o;
+        }
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int l = 0; l < N; ++l) s_tmp[l * NW + wave] = inc[l];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < N; ++l) {
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int c = s_tmp[l * NW + w];
+            before += w < wave ? c : 0;
+            tot += c;
+        }
+        ex[l] = inc[l] - v[l] + before;
+        total[l] = tot;
+    }
+    __syncthreads();
+}
+
 template <typename T>
 __device__ __forceinline__ T load_agent(const T* a) {
     return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -238,12 +275,12 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
         const int groups = cnt > kSmallMax ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
         const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn,
                                      groups * p.tiles_dn * pdn};
+        int ex[N_LISTS], tot[N_LISTS];
+        block_excl_scan_n<N_LISTS>(nitems, s_tmp, ex, tot);
 #pragma unroll
         for (int l = 0; l < N_LISTS; ++l) {
-            int tot;
-            const int ex = block_excl_scan(nitems[l], s_tmp, &tot);
-            if (pos < npos) p.ws.prefix[l * stride + pos] = carry[l] + ex;
-            carry[l] += tot;
+            if (pos < npos) p.ws.prefix[l * stride + pos] = carry[l] + ex[l];
+            carry[l] += tot[l];
         }
     }
     if (tid == 0) {
@@ -318,7 +355,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     const int d = p.d, E = p.E, k = p.k;
     const int nb = (E + NW * EW - 1) / (NW * EW);
     const int t = blockIdx.x / nb, eb = blockIdx.x - t * nb;
-    __shared__ long long s_ex[PW_MAX_EXPERTS];
+    __shared__ long long s_ex[PW_MAX_EXPERTS + 8];   // + sentinels: the rank loop reads 8 at a time
     __shared__ long long s_selv[PW_MAX_TOP_K];
     __shared__ int s_sele[PW_MAX_TOP_K];
     __shared__ int s_last;
@@ -327,7 +364,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __shared__ int s_off[PW_MAX_EXPERTS + 1];
     __shared__ int s_run[PW_MAX_EXPERTS];
     __shared__ int s_wc[NW * PW_MAX_EXPERTS];
-    __shared__ int s_tmp[NW];
+    __shared__ int s_tmp[N_LISTS * NW];
 
     // ---- exact logits of this work-group's experts; y = 0 for the token
     if (eb == 0) {
@@ -366,11 +403,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     // ---- token t: exact top-k by rank (number of experts ahead in key order)
     if (tid == 0) store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
     for (int i = tid; i < E; i += kRouteThreads) s_ex[i] = load_agent(p.ws.lg + (size_t)t * E + i);
+    // below every logit (|logit| < 2^63 by the range check): never ahead in key order
+    if (tid < 8) s_ex[E + tid] = LLONG_MIN;
     __syncthreads();
     if (tid < E) {
         const long long v = s_ex[tid];
         int rank = 0;
-        for (int e2 = 0; e2 < E; ++e2) rank += key_gt(s_ex[e2], e2, v, tid) ? 1 : 0;
+        // eight LDS reads in flight per step instead of one dependent read per expert
+        for (int e0 = 0; e0 < E; e0 += 8) {
+            long long w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = s_ex[e0 + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rank += key_gt(w[j], e0 + j, v, tid) ? 1 : 0;
+        }
         if (rank < k) {
             s_selv[rank] = v;
             s_sele[rank] = tid;
