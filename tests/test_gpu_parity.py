@@ -208,6 +208,21 @@ def test_all_bitwidths_shared_and_ragged(torch_dev):
     run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
 
 
+TWO_GROUPS = synth.MoEConfig("gtwo", 93, d=256, E=4, F=384, k=2, T=32, Fs=512,
+                             bits_rule="uniform", bits_values=(3, 4, 5, 6, 8))
+
+
+def test_two_token_groups_one_kernel(torch_dev):
+    """T = 32: experts with 17..32 tokens (and the 32-token shared expert) run as two
+    16-token groups in the one-tile kernel; no 64-token launch."""
+    cfg = TWO_GROUPS
+    bits = synth.initial_bits(cfg)
+    blocks = synth.make_layer_blocks(cfg, bits)
+    x, wr, bias = layer_inputs(cfg)
+    _, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
+    assert ((ref["counts"] > 16) & (ref["counts"] <= 32)).any(), ref["counts"]
+
+
 def test_t0_noop_and_max_tokens(torch_dev):
     torch, dev = torch_dev
     cfg = synth.CONFIGS["c0"]
