@@ -929,7 +929,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                         const half8 a1 = lut_fragment(rw1, m, slot, 2);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
-                            if (nt < ntl) {
+                            if (NT == 1 || nt < ntl) {   // a one-tile item always holds a token
                                 acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[nt][m], acc0[nt], 0, 0, 0);
                                 acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[nt][m], acc1[nt], 0, 0, 0);
                             }
