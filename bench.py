@@ -10,7 +10,8 @@ on-chip caches and the weights stream from HBM.
 
 Prints one JSON line on stdout; diagnostics go to stderr. With --sweep it
 instead times one layer forward of every workload shape (c0, c1, c2 at T=1 and
-T=64, c3, one c4 layer at T=256) and prints a markdown table.
+T=64, c3, one c4 layer at T=256) and prints a markdown table; with --c4-stack it
+times the whole 24-layer c4 stack over its 64 steps and plan rewrites.
 """
 from __future__ import annotations
 
@@ -134,6 +135,111 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
               f"{100 * gbs / HBM_PEAK_GBS:.1f} | {tps:,.0f} |", flush=True)
 
 
+def c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
+    """The whole c4 workload: 24 layers, each with its own seeded weights, router and pages, over 64
+    decode steps of 256 tokens. Before steps 16, 32 and 48 every layer's plan is rewritten (45 seeded
+    blocks lose two bits, not below 3) and the changed blocks are rebound to their lower planes and
+    LUTs. Every layer also writes its residual x + y. With these synthetic weights a free-running
+    residual chain grows past the exact router's input range within five layers, so each layer takes
+    its own seeded N(0, 1) input per step (independent inputs per step and layer). One HIP event pair
+    on the launch stream brackets each step, rewrite calls included. Algorithmic bytes per layer are
+    read back after the last step of each plan epoch."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cfg = synth.CONFIGS["c4"]
+    T, L, every = cfg.T, cfg.layers, cfg.rewrite_every
+    stream = torch.cuda.current_stream(dev)
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    def reachable(b):   # bitwidths a block at b can reach under the rewrites
+        out = {b}
+        for _ in range(cfg.steps // every):
+            b = max(3, b - 2)
+            out.add(b)
+        return tuple(sorted(out))
+
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        bits = synth.initial_bits(cfg, layer=l)
+        jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+
+        def one(job, l=l, bits=bits):
+            e, lin = job
+            b = int(bits[e, lin])
+            return synth.make_block(cfg, e, lin, layer=l, n_planes=b, lut_bits=reachable(b))
+
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            blocks = list(ex.map(one, jobs))
+        pages = {}
+        for blk in blocks:
+            pages[(blk.e, blk.lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes)).to(dev),
+                                       {b: f16(lut_page(v)) for b, v in blk.luts.items()})
+        del blocks
+        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, T)
+        lay.plan_set(bits)
+        for (e, lin), (p, luts) in pages.items():
+            b = int(bits[e, lin])
+            lay.bind(e, lin, [p[i] for i in range(b)], luts[b], b)
+        wr_h, _ = synth.router(cfg, layer=l)
+        layers.append(dict(bits=bits, pages=pages, lay=lay, wr=f16(wr_h)))
+        log(f"c4 layer {l}: pages ready ({time.time() - t0:.0f}s)")
+    xs = [[f16(synth.tokens(cfg, T, step=s, layer=l)) for l in range(L)] for s in range(cfg.steps)]
+    log(f"c4 inputs ready ({time.time() - t0:.0f}s)")
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+    x_next = torch.empty((T, cfg.d), dtype=torch.float16, device=dev)
+
+    def step(s):
+        if s > 0 and s % every == 0:
+            for l, Ly in enumerate(layers):
+                new, changed = synth.rewrite_plan(cfg, Ly["bits"], layer=l, epoch=s // every)
+                Ly["bits"] = new
+                Ly["lay"].plan_set(new)
+                for blk in changed:
+                    e, lin = divmod(int(blk), 3)
+                    p, luts = Ly["pages"][(e, lin)]
+                    b = int(new[e, lin])
+                    Ly["lay"].bind(e, lin, [p[i] for i in range(b)], luts[b], b)
+        for l, Ly in enumerate(layers):
+            Ly["lay"].forward(xs[s][l], Ly["wr"], None, y=y, x_next=x_next, stream=stream)
+
+    # warm-up: the first steps of the first epoch, on their own copy of the plan state
+    for s in range(min(args.warmup, 2)):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cfg.steps)]
+    epoch_bytes = []
+    for s in range(cfg.steps):
+        evs[s][0].record(stream)
+        step(s)
+        evs[s][1].record(stream)
+        if (s + 1) % every == 0 or s + 1 == cfg.steps:
+            nb = [Ly["lay"].last_bytes(stream) for Ly in layers]
+            epoch_bytes.append((float(np.mean([sum(b[:3]) for b in nb])),
+                                float(np.mean([Ly["bits"].mean() for Ly in layers]))))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    print("| c4 stack epoch | steps | mean bits | algorithmic MB per layer | mean step ms | per-layer us | "
+          "GB/s | HBM % | stack tokens/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    n_ep = (cfg.steps + every - 1) // every
+    for ep in range(n_ep):
+        sl = ms[ep * every:(ep + 1) * every]
+        mb, bits_mean = epoch_bytes[ep]
+        per_layer_us = sl.mean() * 1e3 / L
+        print(f"| {ep} | {ep * every}..{min(cfg.steps, (ep + 1) * every) - 1} | {bits_mean:.2f} | {mb / 1e6:.1f} | "
+              f"{sl.mean():.2f} | {per_layer_us:.1f} | {mb / (per_layer_us * 1e-6) / 1e9:.0f} | "
+              f"{100 * mb / (per_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.1f} | {T / (sl.mean() * 1e-3):,.0f} |")
+    print(f"| all | 0..{cfg.steps - 1} | | | {ms.mean():.2f} | {ms.mean() * 1e3 / L:.1f} | | | "
+          f"{T * cfg.steps / (ms.sum() * 1e-3):,.0f} |", flush=True)
+    for Ly in layers:
+        assert Ly["lay"].status() == 0, "layer status flag set"
+        Ly["lay"].close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +250,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload shape (per-call median, p10, p90) and print a table")
+    ap.add_argument("--c4-stack", action="store_true",
+                    help="time the 24-layer c4 stack over 64 steps with plan rewrites and print a table")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -171,6 +279,9 @@ def main():
         return
     if args.sweep:
         sweep(args, torch, synth, PagedMoELayer, lut_page, dev)
+        return
+    if args.c4_stack:
+        c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev)
         return
     cfg = synth.CONFIGS["c1"]
     T = cfg.T
