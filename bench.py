@@ -9,9 +9,10 @@ clones of the pages at distinct addresses so that the working set exceeds the
 on-chip caches and the weights stream from HBM.
 
 Prints one JSON line on stdout; diagnostics go to stderr. With --sweep it
-instead times one layer forward of every workload shape (c0, c1, c2 at T=1 and
-T=64, c3, one c4 layer at T=256) and prints a markdown table; with --c4-stack it
-times the whole 24-layer c4 stack over its 64 steps and plan rewrites.
+instead times one layer forward of every workload shape (tiny_d256, qwen_d2048_t16,
+mixtral_d4096 at T=1 and T=64, fine_e128_t128, one layer of qwen_stack24_t256) and
+prints a markdown table; with --stack it times the whole 24-layer qwen_stack24_t256
+workload over its 64 steps and plan rewrites.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ def log(*a):
 
 
 KERNEL_SRC = os.path.join(ROOT, "any_precision_bit_amd", "csrc", "pw_kernels.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_kernel_c1_decode_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_kernel_qwen_d2048_t16_traffic.md")
 
 
 def kernel_code_digest():
@@ -58,9 +59,11 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
-# (label, config, tokens or None for the config's own, rotation clones); c0 is cache-resident
-SWEEP = [("c0", "c0", None, 1), ("c1", "c1", None, 8), ("c2 T=1", "c2", 1, 8), ("c2 T=64", "c2", 64, 4),
-         ("c3", "c3", None, 4), ("c4 layer 0, T=256, first plan", "c4", None, 4)]
+# (label, workload, tokens or None for the workload's own, rotation clones); tiny_d256 is cache-resident
+SWEEP = [("tiny_d256", "tiny_d256", None, 1), ("qwen_d2048_t16", "qwen_d2048_t16", None, 8),
+         ("mixtral_d4096 T=1", "mixtral_d4096", 1, 8), ("mixtral_d4096 T=64", "mixtral_d4096", 64, 4),
+         ("fine_e128_t128", "fine_e128_t128", None, 4),
+         ("qwen_stack24_t256 layer 0, first plan", "qwen_stack24_t256", None, 4)]
 
 
 def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
@@ -135,8 +138,8 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
               f"{100 * gbs / HBM_PEAK_GBS:.1f} | {tps:,.0f} |", flush=True)
 
 
-def c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
-    """The whole c4 workload: 24 layers, each with its own seeded weights, router and pages, over 64
+def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
+    """The whole qwen_stack24_t256 workload: 24 layers, each with its own seeded weights, router and pages, over 64
     decode steps of 256 tokens. Before steps 16, 32 and 48 every layer's plan is rewritten (45 seeded
     blocks lose two bits, not below 3) and the changed blocks are rebound to their lower planes and
     LUTs. Every layer also writes its residual x + y. With these synthetic weights a free-running
@@ -146,7 +149,7 @@ def c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
     read back after the last step of each plan epoch."""
     from concurrent.futures import ThreadPoolExecutor
 
-    cfg = synth.CONFIGS["c4"]
+    cfg = synth.CONFIGS["qwen_stack24_t256"]
     T, L, every = cfg.T, cfg.layers, cfg.rewrite_every
     stream = torch.cuda.current_stream(dev)
 
@@ -186,9 +189,9 @@ def c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
             lay.bind(e, lin, [p[i] for i in range(b)], luts[b], b)
         wr_h, _ = synth.router(cfg, layer=l)
         layers.append(dict(bits=bits, pages=pages, lay=lay, wr=f16(wr_h)))
-        log(f"c4 layer {l}: pages ready ({time.time() - t0:.0f}s)")
+        log(f"stack layer {l}: pages ready ({time.time() - t0:.0f}s)")
     xs = [[f16(synth.tokens(cfg, T, step=s, layer=l)) for l in range(L)] for s in range(cfg.steps)]
-    log(f"c4 inputs ready ({time.time() - t0:.0f}s)")
+    log(f"stack inputs ready ({time.time() - t0:.0f}s)")
     y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
     x_next = torch.empty((T, cfg.d), dtype=torch.float16, device=dev)
 
@@ -222,7 +225,7 @@ def c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
                                 float(np.mean([Ly["bits"].mean() for Ly in layers]))))
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in evs])
-    print("| c4 stack epoch | steps | mean bits | algorithmic MB per layer | mean step ms | per-layer us | "
+    print("| plan epoch | steps | mean bits | algorithmic MB per layer | mean step ms | per-layer us | "
           "GB/s | HBM % | stack tokens/s |")
     print("|---|---|---|---|---|---|---|---|---|")
     n_ep = (cfg.steps + every - 1) // every
@@ -250,8 +253,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload shape (per-call median, p10, p90) and print a table")
-    ap.add_argument("--c4-stack", action="store_true",
-                    help="time the 24-layer c4 stack over 64 steps with plan rewrites and print a table")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the 24-layer qwen_stack24_t256 workload over 64 steps with plan rewrites")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -280,17 +283,17 @@ def main():
     if args.sweep:
         sweep(args, torch, synth, PagedMoELayer, lut_page, dev)
         return
-    if args.c4_stack:
-        c4_stack(args, torch, synth, PagedMoELayer, lut_page, dev)
+    if args.stack:
+        layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev)
         return
-    cfg = synth.CONFIGS["c1"]
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
     T = cfg.T
     t0 = time.time()
     bits = synth.initial_bits(cfg)
     blocks = synth.make_layer_blocks(cfg, bits)
     x_h = synth.tokens(cfg)
     wr_h, _ = synth.router(cfg)
-    log(f"generated c1 pages in {time.time() - t0:.1f}s")
+    log(f"generated qwen_d2048_t16 pages in {time.time() - t0:.1f}s")
 
     def f16(a):
         return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
@@ -382,7 +385,7 @@ def main():
             n_tok += T
             reps += 1
         cpu = {"value": round(n_tok / t_cpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"{reps} full forward(s) of the same 16-token c1 batch ({n_tok} tokens), "
+               "sample": f"{reps} full forward(s) of the same 16-token qwen_d2048_t16 batch ({n_tok} tokens), "
                          f"{t_cpu:.1f}s on {threads} threads"}
         log(f"oracle: {cpu['value']} tokens/s on {threads} threads")
 

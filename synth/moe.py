@@ -85,27 +85,27 @@ class MoEConfig:
 # The five workloads: shapes follow the pages' evaluation models
 # (legiblepapers FAQ Q6: Qwen1.5-MoE-A2.7B, Mixtral-8x7B-v0.1) at synthetic values.
 CONFIGS = {
-    "c0": MoEConfig("c0", 0, d=256, E=8, F=512, k=2, T=4,
+    "tiny_d256": MoEConfig("tiny_d256", 0, d=256, E=8, F=512, k=2, T=4,
                     bits_rule="uniform", bits_values=(3, 4)),
-    "c1": MoEConfig("c1", 1, d=2048, E=60, F=1408, k=4, T=16, Fs=5632,
+    "qwen_d2048_t16": MoEConfig("qwen_d2048_t16", 1, d=2048, E=60, F=1408, k=4, T=16, Fs=5632,
                     bits_rule="uniform", bits_values=(3, 4, 5, 6, 8)),
-    "c2": MoEConfig("c2", 2, d=4096, E=8, F=14336, k=2, T=1,
+    "mixtral_d4096": MoEConfig("mixtral_d4096", 2, d=4096, E=8, F=14336, k=2, T=1,
                     bits_rule="choice", bits_values=(3, 4, 6, 8),
                     bits_probs=(0.3, 0.3, 0.2, 0.2), zipf=1.2),
-    "c3": MoEConfig("c3", 3, d=2048, E=128, F=768, k=8, T=128,
+    "fine_e128_t128": MoEConfig("fine_e128_t128", 3, d=2048, E=128, F=768, k=8, T=128,
                     bits_rule="frequency", bits_values=(8, 4, 3), zipf=1.1),
-    "c4": MoEConfig("c4", 4, d=2048, E=60, F=1408, k=4, T=256, Fs=5632,
+    "qwen_stack24_t256": MoEConfig("qwen_stack24_t256", 4, d=2048, E=60, F=1408, k=4, T=256, Fs=5632,
                     bits_rule="uniform", bits_values=(3, 4, 5, 6, 8),
                     layers=24, steps=64, rewrite_every=16, rewrite_frac=0.25,
                     rewrite_drop=2),
 }
 
 WORKLOAD_TEXT = {
-    "c0": "d256 E8 F512 top2 T4, bits U{3,4}",
-    "c1": "Qwen1.5-MoE-A2.7B-shaped decode layer: d2048 E60 F1408 top4 T16 + shared F5632, bits U{3,4,5,6,8}",
-    "c2": "Mixtral-8x7B-shaped layer: d4096 E8 F14336 top2, bits {3,4,6,8} p=(.3,.3,.2,.2), Zipf(1.2) routing",
-    "c3": "fine-grained layer: d2048 E128 F768 top8 T128, Zipf(1.1) routing, bits by routed frequency 8/4/3",
-    "c4": "24-layer stack of the d2048 E60 F1408 top4 (+shared F5632) layer, T256, 64 steps, plan rewrite every 16",
+    "tiny_d256": "d256 E8 F512 top2 T4, bits U{3,4}",
+    "qwen_d2048_t16": "Qwen1.5-MoE-A2.7B-shaped decode layer: d2048 E60 F1408 top4 T16 + shared F5632, bits U{3,4,5,6,8}",
+    "mixtral_d4096": "Mixtral-8x7B-shaped layer: d4096 E8 F14336 top2, bits {3,4,6,8} p=(.3,.3,.2,.2), Zipf(1.2) routing",
+    "fine_e128_t128": "fine-grained layer: d2048 E128 F768 top8 T128, Zipf(1.1) routing, bits by routed frequency 8/4/3",
+    "qwen_stack24_t256": "24-layer stack of the d2048 E60 F1408 top4 (+shared F5632) layer, T256, 64 steps, plan rewrite every 16",
 }
 
 

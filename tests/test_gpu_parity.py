@@ -89,18 +89,18 @@ def _blocks(cfg, bits, **kw):
     return synth.make_layer_blocks(cfg, bits, **kw)
 
 
-def test_c0_full(torch_dev):
-    cfg = synth.CONFIGS["c0"]
-    _say("c0")
+def test_tiny_full(torch_dev):
+    cfg = synth.CONFIGS["tiny_d256"]
+    _say("tiny_d256")
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     x, wr, bias = layer_inputs(cfg)
     run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
 
 
-def test_c1_full(torch_dev):
-    cfg = synth.CONFIGS["c1"]
-    _say("c1")
+def test_qwen_decode_full(torch_dev):
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    _say("qwen_d2048_t16")
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     x, wr, bias = layer_inputs(cfg)
@@ -109,23 +109,23 @@ def test_c1_full(torch_dev):
 
 @pytest.fixture(scope="module")
 def c2_data():
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["mixtral_d4096"]
     bits = synth.initial_bits(cfg)
     return cfg, bits, _blocks(cfg, bits)
 
 
 @pytest.mark.parametrize("T,n_check", [(1, 1), (64, 8)])
-def test_c2(torch_dev, c2_data, T, n_check):
+def test_mixtral(torch_dev, c2_data, T, n_check):
     cfg, bits, blocks = c2_data
-    _say(f"c2 T={T}")
+    _say(f"mixtral_d4096 T={T}")
     cfgT = cfg.with_tokens(T)
     x, wr, bias = layer_inputs(cfgT)
     run_parity(torch_dev, cfgT, bits, blocks, x, wr, bias, sample_tokens(T, n_check, seed=T))
 
 
-def test_c3(torch_dev):
-    cfg = synth.CONFIGS["c3"]
-    _say("c3")
+def test_fine_e128(torch_dev):
+    cfg = synth.CONFIGS["fine_e128_t128"]
+    _say("fine_e128_t128")
     x, wr, bias = layer_inputs(cfg)
     L, _ = oracle.router_logits(x, wr, bias)
     ids, _ = oracle.topk_softmax(L, cfg.k)
@@ -136,7 +136,7 @@ def test_c3(torch_dev):
     assert ref["counts"].max() > 32          # exercises the multi-tile (large) kernels
 
 
-def test_c4_stack_teacher_forced(torch_dev):
+def test_qwen_stack_teacher_forced(torch_dev):
     """A 3-layer slice of the 24-layer stack, 64 decode steps at T=256 with the
     plan rewritten (and pages rebound) before steps 16, 32 and 48. Every step
     runs on the GPU; routing is checked in full and outputs on 4 sampled tokens
@@ -144,7 +144,7 @@ def test_c4_stack_teacher_forced(torch_dev):
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
-    cfg = synth.CONFIGS["c4"]
+    cfg = synth.CONFIGS["qwen_stack24_t256"]
     n_layers, T = 3, cfg.T
     layers = []
     for l in range(n_layers):
@@ -181,7 +181,7 @@ def test_c4_stack_teacher_forced(torch_dev):
                 ref = L["orc"].forward(xh, L["wr"], None, subset=sub)
                 check_routing(route, ref, T, cfg.E, cfg.k)
                 err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
-                _say(f"c4 step {s} layer {l}: max rel err {err.max():.3e}")
+                _say(f"qwen_stack24_t256 step {s} layer {l}: max rel err {err.max():.3e}")
                 assert err.max() <= REL_TOL
                 xn_ref = oracle.residual(xh, y.cpu().numpy())   # O9 on the GPU's own y
                 assert np.array_equal(f16_host(x_next).view(np.uint16), xn_ref.view(np.uint16))
@@ -225,7 +225,7 @@ def test_two_token_groups_one_kernel(torch_dev):
 
 def test_t0_noop_and_max_tokens(torch_dev):
     torch, dev = torch_dev
-    cfg = synth.CONFIGS["c0"]
+    cfg = synth.CONFIGS["tiny_d256"]
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     pages = device_pages(blocks, bits, dev)
@@ -243,7 +243,7 @@ def test_ties_zero_input_and_determinism(torch_dev):
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
-    cfg = synth.CONFIGS["c0"].with_tokens(16)
+    cfg = synth.CONFIGS["tiny_d256"].with_tokens(16)
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     x, wr, _ = layer_inputs(cfg)
@@ -264,7 +264,7 @@ def test_ties_zero_input_and_determinism(torch_dev):
 
 def test_plan_rewrite_and_rebind(torch_dev):
     torch, dev = torch_dev
-    cfg = synth.CONFIGS["c1"].with_tokens(8)
+    cfg = synth.CONFIGS["qwen_d2048_t16"].with_tokens(8)
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits, all_luts=True)
     pages = device_pages(blocks, bits, dev, all_luts=True)
@@ -282,7 +282,7 @@ def test_plan_rewrite_and_rebind(torch_dev):
 
 def test_router_range_flag(torch_dev):
     torch, dev = torch_dev
-    cfg = synth.CONFIGS["c0"]
+    cfg = synth.CONFIGS["tiny_d256"]
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     lay = gpu_layer(cfg, bits, device_pages(blocks, bits, dev))

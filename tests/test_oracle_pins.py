@@ -68,7 +68,7 @@ def test_index_uses_only_top_planes():
 
 
 def test_b8_reproduces_parent_dequant():
-    cfg = synth.CONFIGS["c0"]
+    cfg = synth.CONFIGS["tiny_d256"]
     for lin in (GATE, DOWN):
         q = synth.parent_indices(cfg, 2, lin)
         planes = synth.pack_planes(q)
@@ -79,7 +79,7 @@ def test_b8_reproduces_parent_dequant():
 
 
 def test_dequant_bitwidth_b_matches_truncated_parent():
-    cfg = synth.CONFIGS["c0"]
+    cfg = synth.CONFIGS["tiny_d256"]
     q = synth.parent_indices(cfg, 1, UP)
     planes = synth.pack_planes(q)
     for b in (3, 4, 5, 6, 8):
@@ -137,10 +137,10 @@ def test_golden_router_fixture():
     assert srt.tolist() == g["sorted"]
 
 
-@pytest.mark.parametrize("cname", ["c0", "c2"])
+@pytest.mark.parametrize("cname", ["tiny_d256", "mixtral_d4096"])
 def test_router_exact_vs_python_int(cname):
     cfg = synth.CONFIGS[cname]
-    if cname == "c2":
+    if cname == "mixtral_d4096":
         # a slice of the Zipf-biased Mixtral-shaped router, exercising the bias term
         wr, bias = synth.router(cfg)
         wr = wr[:, :512]
@@ -176,7 +176,7 @@ def test_topk_and_bucket_sort_bruteforce():
 
 
 def test_topk_all_experts_and_identical_rows():
-    cfg = synth.CONFIGS["c0"]
+    cfg = synth.CONFIGS["tiny_d256"]
     x = synth.tokens(cfg)
     wr, _ = synth.router(cfg)
     wr = wr.copy()
@@ -250,7 +250,7 @@ def rel_err_per_token(y, ref):
     return num / np.maximum(den, 1e-30)
 
 
-@pytest.mark.parametrize("cfg", [synth.CONFIGS["c0"], SMALL], ids=["c0", "small_shared"])
+@pytest.mark.parametrize("cfg", [synth.CONFIGS["tiny_d256"], SMALL], ids=["tiny_d256", "small_shared"])
 def test_whole_layer_vs_dense_fp64(cfg):
     bits = synth.initial_bits(cfg)
     blocks = synth.make_layer_blocks(cfg, bits, keep_parent=True)
@@ -353,7 +353,7 @@ def test_plan_change_is_stateless():
 
 
 def test_rewrite_plan_rule():
-    cfg = synth.CONFIGS["c4"]
+    cfg = synth.CONFIGS["qwen_stack24_t256"]
     bits = synth.initial_bits(cfg, layer=3)
     assert bits.shape == (61, 3)
     new, changed = synth.rewrite_plan(cfg, bits, layer=3, epoch=1)
