@@ -447,7 +447,8 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
 
     for (int phase = 0; phase < 3; ++phase)
         if ((st = launch_phase(L, phase, s)) != PW_OK) return st;
-    if (getenv("PW_DEBUG_SYNC")) {
+    static const bool debug_sync = getenv("PW_DEBUG_SYNC") != nullptr;   // read once per process
+    if (debug_sync) {
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, "pw_moe_forward (debug sync)");
     }

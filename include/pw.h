@@ -138,7 +138,9 @@ pw_status pw_page_table_bind(pw_layer layer, int32_t expert, int32_t linear,
  * That needs |x|, |router_w| < 128 and sum_c |x*w| + |b| < 2^15 per (token,
  * expert); a token/expert outside that range sets PW_STATUS_ROUTER_RANGE in the
  * device status word (read with pw_layer_status) and its routing is undefined.
- * T == 0 is a no-op. */
+ * T == 0 is a no-op. With the environment variable PW_DEBUG_SYNC set (read once
+ * per process) the call synchronises `stream` before returning, so that a
+ * kernel fault surfaces here as PW_E_HIP. */
 pw_status pw_moe_forward(pw_layer layer, const void* x, int32_t T, const void* router_w,
                          const void* router_b, float* y, void* x_next,
                          const pw_route_out* route, void* stream);
