@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libpw.so")
 PW_ABI_VERSION = 1
 PW_GATE, PW_UP, PW_DOWN = 0, 1, 2
 PW_STATUS_ROUTER_RANGE = 1
+PW_STATUS_DEP_TIMEOUT = 2
 STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "PW_E_UNBOUND",
                 5: "PW_E_ALIGN", 6: "PW_E_RANGE", 7: "PW_E_STATE", 8: "PW_E_NOMEM", 9: "PW_E_HIP"}
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
             "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
-            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant"]
+            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit"]
 
 
 class PwError(RuntimeError):
@@ -68,6 +69,7 @@ def _load():
         "pw_layer_last_bytes": ([P, P, ctypes.POINTER(ctypes.c_double)], st),
         "pw_debug_unpack": ([P, i32, i32, i32, P, P], st),
         "pw_debug_dequant": ([P, i32, P, i32, i32, P, P], st),
+        "pw_debug_set_wait_limit": ([P, u32], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -145,3 +147,7 @@ def pw_debug_unpack(planes, b: int, R: int, K: int, idx_out: int, stream: int = 
 def pw_debug_dequant(planes, b: int, lut: int, R: int, K: int, w_out: int, stream: int = 0) -> None:
     arr = (ctypes.c_void_p * 8)(*([int(p) for p in planes] + [None] * (8 - len(planes))))
     _check(lib.pw_debug_dequant(arr, b, lut, R, K, w_out, stream or None))
+
+
+def pw_debug_set_wait_limit(layer: int, polls: int) -> None:
+    _check(lib.pw_debug_set_wait_limit(layer, polls))

@@ -95,6 +95,7 @@ struct pw_layer_s {
 
     // launch record of the last forward (for pw_layer_last_bytes and pw_moe_replay)
     int last_T = 0;
+    uint32_t wait_limit = 1u << 20;   // polls of a down item's dependency counter
     pw::RouteParams rp{};
     pw::GemmParams gp_gu{}, gp_dn{};
     const uint16_t* res_x = nullptr;
@@ -147,7 +148,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     const size_t o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
     const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
     const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
-    const size_t o_st = off;     off += al(sizeof(uint32_t));
+    const size_t o_st = off;     off += al(2 * sizeof(uint32_t));   // status, wait limit
     const size_t o_lg = off;     off += al(sizeof(long long) * (size_t)T * E);
     const int dep_stride = (L->f_max + pw::kDownPiece - 1) / pw::kDownPiece;
     const int n_dep = (E + 1) * dep_stride + 1;
@@ -179,6 +180,7 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     L->ws.prefix = (int32_t*)(b + o_pre);
     L->ws.act = (uint16_t*)(b + o_act);
     L->ws.status = (uint32_t*)(b + o_st);
+    L->ws.wait_limit = L->ws.status + 1;
     L->ws.lg = (long long*)(b + o_lg);
     L->ws.dep = (uint32_t*)(b + o_dep);
     L->ws.tok_cnt = L->ws.dep + n_dep;
@@ -193,7 +195,8 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess)
             return hip_fail(e, "hipEventCreate");
     }
-    if ((e = pw::launch_init_ws(L->ws, n_counters, s)) != hipSuccess) return hip_fail(e, "init workspace");
+    if ((e = pw::launch_init_ws(L->ws, n_counters, L->wait_limit, s)) != hipSuccess)
+        return hip_fail(e, "init workspace");
     L->dev_ready = true;
     return PW_OK;
 }
@@ -483,7 +486,10 @@ pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
             return hip_fail(e, "status clear");
     }
     *flags = v;
-    if (v) return fail(PW_E_STATE, "device status flags 0x%x (router range)", v);
+    if (v)
+        return fail(PW_E_STATE, "device status flags 0x%x (%s%s)", v,
+                    (v & PW_STATUS_ROUTER_RANGE) ? "router range " : "",
+                    (v & PW_STATUS_DEP_TIMEOUT) ? "dependency wait timed out" : "");
     return PW_OK;
 }
 
@@ -553,3 +559,16 @@ pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut
 }
 
 }  // extern "C"
+
+pw_status pw_debug_set_wait_limit(pw_layer L, uint32_t polls) {
+    g_err.clear();
+    if (!L) return fail(PW_E_ARG, "pw_debug_set_wait_limit: null layer");
+    L->wait_limit = polls;
+    if (L->dev_ready) {   // later forwards read it from the workspace
+        DeviceGuard guard(L->device);
+        if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
+        const hipError_t e = hipMemcpy(L->ws.wait_limit, &polls, sizeof polls, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "wait limit");
+    }
+    return PW_OK;
+}

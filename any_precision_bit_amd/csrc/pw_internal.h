@@ -35,6 +35,8 @@ struct Workspace {
     int32_t* prefix;     // [N_LISTS][E+2]
     uint16_t* act;       // [max_T*k + max_T*has_shared][F_max]  SwiGLU output, permuted
     uint32_t* status;    // [1]          PW_STATUS_* bits
+    uint32_t* wait_limit;// [1]          polls of a down item's dependency counter before
+                         //              PW_STATUS_DEP_TIMEOUT (host-written, read-only in kernels)
     long long* lg;       // [max_T][E]   exact router logits, units of 2^-48 (route kernel, between work-groups)
     // counters, contiguous and zeroed once; every launch leaves them at zero
     uint32_t* dep;       // [(E+1)*dep_stride + 1]  gate_up items done per (list position, down
@@ -94,7 +96,7 @@ struct ExpertParams {
     GemmParams dn;
 };
 
-hipError_t launch_init_ws(const Workspace& ws, int n_counters, hipStream_t s);
+hipError_t launch_init_ws(const Workspace& ws, int n_counters, uint32_t wait_limit, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
 // The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).

@@ -862,8 +862,14 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 // every gate_up item of this expert's K-piece has released its act rows
                 const uint32_t need = (uint32_t)((it.klen >> 5) * ((it.n_tok + 16 * NT - 1) / (16 * NT)));
                 const uint32_t* c = dep + it.pos * dstride + it.piece;
-                while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need)
+                uint32_t polls = 0;
+                while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                    if (polls++ >= kconst(g.ws.wait_limit)[0]) {   // bounded: a missing producer becomes a flag
+                        if (tid == 0) atomicOr(g.ws.status, PW_STATUS_DEP_TIMEOUT);
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(1);
+                }
             }
             // the next item: its metadata and token rows now
             const int next = item + (int)gridDim.x;
@@ -1066,8 +1072,11 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
     if (i < n) out[i] = f2h(h2f(x[i]) + y[i]);
 }
 
-__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_counters) {
-    if (threadIdx.x == 0) *ws.status = 0u;
+__global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_counters, uint32_t wait_limit) {
+    if (threadIdx.x == 0) {
+        *ws.status = 0u;
+        *ws.wait_limit = wait_limit;
+    }
     for (int i = threadIdx.x; i < n_counters; i += 64) ws.dep[i] = 0u;   // dep, tok_cnt, route_done
 }
 
@@ -1137,8 +1146,8 @@ int expert_lds_bytes(int tile_tokens) {
     return kStripeBytes + 4 * nt * 4 * 64 * 4 + 2 * kTokWords * 4 + 2 * kPreWords * 4 + 16;
 }
 
-hipError_t launch_init_ws(const Workspace& ws, int n_counters, hipStream_t s) {
-    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws, n_counters);
+hipError_t launch_init_ws(const Workspace& ws, int n_counters, uint32_t wait_limit, hipStream_t s) {
+    hipLaunchKernelGGL(init_ws_kernel, dim3(1), dim3(64), 0, s, ws, n_counters, wait_limit);
     return hipGetLastError();
 }
 

@@ -75,6 +75,10 @@ class PagedMoELayer:
         s = stream if stream is not None else torch.cuda.current_stream()
         B.pw_moe_replay(self.handle, phase, int(s.cuda_stream))
 
+    def set_wait_limit(self, polls: int) -> None:
+        """Test hook: polls of a down item's dependency counter before it gives up."""
+        B.pw_debug_set_wait_limit(self.handle, polls)
+
     def last_bytes(self, stream: Optional[torch.cuda.Stream] = None):
         s = stream if stream is not None else torch.cuda.current_stream()
         return B.pw_layer_last_bytes(self.handle, int(s.cuda_stream))

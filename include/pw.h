@@ -67,6 +67,8 @@ enum { PW_GATE = 0, PW_UP = 1, PW_DOWN = 2 };
 
 /* bits of the device status word read by pw_layer_status */
 #define PW_STATUS_ROUTER_RANGE 1u  /* a token/expert left the exact-router range */
+#define PW_STATUS_DEP_TIMEOUT 2u   /* a down item stopped waiting for its gate_up rows
+                                      (work-groups not all resident); y is undefined */
 
 typedef struct pw_layer_s* pw_layer;  /* opaque; one MoE layer */
 
@@ -174,6 +176,13 @@ pw_status pw_debug_unpack(const void* const* planes, int32_t b, int32_t R, int32
                           uint8_t* idx_out, void* stream);
 pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut, int32_t R,
                            int32_t K, void* w_out, void* stream);
+
+/* Test hook: how many times a down item polls the counter of its gate_up rows
+ * before it gives up, sets PW_STATUS_DEP_TIMEOUT and goes on (later forwards of
+ * this layer; default 1 << 20 polls, about a second). The expert kernel's
+ * work-groups are all resident at once, so the wait ends unless that fails;
+ * the limit turns such a hang into a status flag. PW_E_ARG for a null layer. */
+pw_status pw_debug_set_wait_limit(pw_layer layer, uint32_t polls);
 
 #ifdef __cplusplus
 }

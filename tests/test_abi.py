@@ -153,3 +153,16 @@ def test_status_and_replay_without_device_state(B):
         assert ei.value.status == 7
     finally:
         B.pw_layer_destroy(h)
+
+
+def test_wait_limit_hook(B):
+    with pytest.raises(B.PwError) as ei:
+        B.pw_debug_set_wait_limit(0, 0)               # null layer
+    assert ei.value.status == 1
+    h = B.pw_layer_create(256, 8, 512, 2, 0, 16)
+    try:
+        B.pw_debug_set_wait_limit(h, 0)
+        B.pw_debug_set_wait_limit(h, 1 << 20)
+    finally:
+        B.pw_layer_destroy(h)
+

@@ -191,6 +191,34 @@ def test_qwen_stack_teacher_forced(torch_dev):
         assert L["lay"].status() == 0
 
 
+
+def test_dependency_wait_limit_flags_and_recovers(torch_dev):
+    """With the down items' dependency wait limited to zero polls, a down item that finds its
+    gate_up rows unfinished gives up: the forward still completes, and the status word reports
+    PW_STATUS_DEP_TIMEOUT (every item of this small layer starts in the first round, so the down
+    items poll before their gate_up items can have finished). Back at the default limit the
+    same layer and pages are exact again."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import binding as B
+
+    cfg = synth.CONFIGS["tiny_d256"]
+    bits = synth.initial_bits(cfg)
+    blocks = _blocks(cfg, bits)
+    x, wr, bias = layer_inputs(cfg)
+    pages = device_pages(blocks, bits, dev)
+    lay = gpu_layer(cfg, bits, pages, max_tokens=cfg.T)
+    _say("dependency wait limit 0")
+    lay.set_wait_limit(0)
+    lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev))
+    torch.cuda.synchronize()
+    flags = lay.status()
+    assert flags & B.PW_STATUS_DEP_TIMEOUT, flags
+    assert lay.status() == 0                      # read and cleared
+    lay.set_wait_limit(1 << 20)
+    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32),
+               layer=lay, pages=pages)
+
+
 # ----------------------------------------------------------------------------- edge cases
 SMALL = synth.MoEConfig("gsmall", 92, d=256, E=6, F=384, k=3, T=40, Fs=512,
                         bits_rule="uniform", bits_values=(1, 2, 3, 4, 5, 6, 7, 8))
