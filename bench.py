@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
 
 
 def log(*a):
@@ -67,9 +68,12 @@ SWEEP = [("tiny_d256", "tiny_d256", None, 1), ("qwen_d2048_t16", "qwen_d2048_t16
 
 
 def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
-    """Per-call times of one layer forward (routing + experts) for every workload shape:
-    warm-up calls, then timed calls each bracketed by HIP events on the launch stream,
-    rotating over byte-identical page clones."""
+    """Per-call times of one layer forward (routing + experts) for every workload shape (or the one
+    labelled --only): warm-up calls, then timed calls each bracketed by HIP events on the launch
+    stream, rotating over byte-identical page clones. Useful MFMA work is the dense-equivalent
+    2 * tokens * rows * K of every (expert, linear) over the tokens routed to it (and all T for the
+    shared expert), from the routed counts of one more forward."""
+    from any_precision_bit_amd import route_buffers
     def f16(a):
         return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
             torch.float16)
@@ -77,6 +81,8 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
     rows = []
     stream = torch.cuda.current_stream(dev)
     for label, key, T, M in SWEEP:
+        if args.only and label != args.only:
+            continue
         cfg = synth.CONFIGS[key]
         if T is not None:
             cfg = cfg.with_tokens(T)
@@ -123,19 +129,27 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
         us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
         nb = lays[0][0].last_bytes(stream)
         layer_bytes = nb[0] + nb[1] + nb[2]
+        route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+        lays[0][0].forward(x, wr, bias, y=lays[0][2], route=route, stream=stream)
+        torch.cuda.synchronize()
+        counts = route["expert_count"].cpu().numpy().astype(np.float64)
+        flops = 2.0 * 3 * cfg.F * cfg.d * counts.sum() + (2.0 * 3 * cfg.Fs * cfg.d * cfg.T if cfg.Fs else 0.0)
         med = float(np.median(us))
         rows.append((label, cfg.T, M, layer_bytes / 1e6, med, float(np.percentile(us, 10)),
-                     float(np.percentile(us, 90)), layer_bytes / (med * 1e-6) / 1e9, cfg.T / (med * 1e-6)))
+                     float(np.percentile(us, 90)), layer_bytes / (med * 1e-6) / 1e9, cfg.T / (med * 1e-6),
+                     flops / (med * 1e-6) / 1e12))
         log(f"{label}: median {med:.1f} us")
         for lay, _, _ in lays:
             lay.close()
         del lays, base
         torch.cuda.empty_cache()
-    print("| workload | T | clones | algorithmic MB | median us | p10 us | p90 us | GB/s | HBM % | tokens/s |")
-    print("|---|---|---|---|---|---|---|---|---|---|")
-    for label, T, M, mb, med, p10, p90, gbs, tps in rows:
+    print("| workload | T | clones | algorithmic MB | median us | p10 us | p90 us | GB/s | HBM % | tokens/s | "
+          "useful MFMA TFLOP/s | % of fp16 MFMA peak |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for label, T, M, mb, med, p10, p90, gbs, tps, tf in rows:
         print(f"| {label} | {T} | {M} | {mb:.1f} | {med:.1f} | {p10:.1f} | {p90:.1f} | {gbs:.0f} | "
-              f"{100 * gbs / HBM_PEAK_GBS:.1f} | {tps:,.0f} |", flush=True)
+              f"{100 * gbs / HBM_PEAK_GBS:.1f} | {tps:,.0f} | {tf:.1f} | {100 * tf / MFMA_F16_PEAK_TFLOPS:.2f} |",
+              flush=True)
 
 
 def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
@@ -253,6 +267,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload shape (per-call median, p10, p90) and print a table")
+    ap.add_argument("--only", default="", metavar="LABEL",
+                    help="with --sweep: time only the workload of this label (e.g. 'mixtral_d4096 T=64')")
     ap.add_argument("--stack", action="store_true",
                     help="time the 24-layer qwen_stack24_t256 workload over 64 steps with plan rewrites")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
