@@ -264,7 +264,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--clones", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload shape (per-call median, p10, p90) and print a table")
     ap.add_argument("--only", default="", metavar="LABEL",
@@ -394,7 +394,7 @@ def main():
         cores = len(os.sched_getaffinity(0))
         threads = min(cores, 16)
         n_tok, t_cpu, reps = 0, 0.0, 0
-        while t_cpu < args.cpu_seconds and reps < 8:
+        while t_cpu < args.cpu_seconds and reps < 32:
             tt = time.perf_counter()
             lay_o.forward(x_h, wr_h, None, threads=threads)
             t_cpu += time.perf_counter() - tt
