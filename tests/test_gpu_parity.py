@@ -219,6 +219,84 @@ def test_dependency_wait_limit_flags_and_recovers(torch_dev):
                layer=lay, pages=pages)
 
 
+
+def test_qwen_stack_all_layers_independent_inputs(torch_dev):
+    """All 24 layers of the stack at T=256, with the plan rewritten (and pages rebound) before steps
+    16, 32 and 48, in the configuration `bench.py --stack` times: each layer takes its own seeded
+    input per step. The steps on both sides of each rewrite run: routing is checked on every token
+    of every layer, and outputs on one sampled token of a quarter of the layers (rotating) at the
+    first step of each plan epoch. A forward leaves no state behind but the plan and the pages, so
+    the steps in between, which only repeat the same kernels, are skipped."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import route_buffers
+
+    from concurrent.futures import ThreadPoolExecutor
+
+    cfg = synth.CONFIGS["qwen_stack24_t256"]
+    T = cfg.T
+
+    def reachable(b):   # bitwidths a block at b passes through under the rewrites
+        out = {b}
+        for _ in range(cfg.steps // cfg.rewrite_every):
+            b = max(3, b - 2)
+            out.add(b)
+        return tuple(sorted(out))
+
+    def stack_blocks(bits, l):   # planes 0..b-1 and the LUTs of every reachable bitwidth
+        jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            made = list(ex.map(lambda j: synth.make_block(cfg, j[0], j[1], layer=l, n_planes=int(bits[j]),
+                                                          lut_bits=reachable(int(bits[j]))), jobs))
+        return {(blk.e, blk.lin): blk for blk in made}
+
+    layers = []
+    for l in range(cfg.layers):
+        bits = synth.initial_bits(cfg, layer=l)
+        blocks = stack_blocks(bits, l)
+        pages = device_pages(blocks, bits, dev, all_luts=True)
+        lay = gpu_layer(cfg, bits, pages, max_tokens=T)
+        wr, _ = synth.router(cfg, layer=l)
+        layers.append(dict(bits=bits, pages=pages, lay=lay, wr=wr, wd=to_dev_f16(wr, dev),
+                           orc=oracle.OracleLayer.from_config(cfg, bits, blocks)))
+    _say(f"stack: {cfg.layers} layers ready")
+    check_steps = {0, 15, 16, 31, 32, 47, 48, 63}
+    route = route_buffers(T, cfg.E, cfg.k, dev)
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+    x_next = torch.empty((T, cfg.d), dtype=torch.float16, device=dev)
+    worst = 0.0
+    for s in range(cfg.steps):
+        if s > 0 and s % cfg.rewrite_every == 0:
+            for l, L in enumerate(layers):
+                new, changed = synth.rewrite_plan(cfg, L["bits"], layer=l, epoch=s // cfg.rewrite_every)
+                L["bits"] = new
+                L["lay"].plan_set(new)
+                for blk in changed:
+                    e, lin = divmod(int(blk), 3)
+                    planes, luts = L["pages"][(e, lin)]
+                    b = int(new[e, lin])
+                    L["lay"].bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
+                L["orc"].set_bits(new)
+        if s not in check_steps:
+            continue
+        epoch = s // cfg.rewrite_every
+        for l, L in enumerate(layers):
+            x = synth.tokens(cfg, T, step=s, layer=l)
+            L["lay"].forward(to_dev_f16(x, dev), L["wd"], None, y=y, x_next=x_next, route=route)
+            torch.cuda.synchronize()
+            outputs = s % cfg.rewrite_every == 0 and l % 4 == epoch % 4
+            sub = sample_tokens(T, 1, seed=1000 * s + l) if outputs else np.zeros(0, dtype=np.int32)
+            ref = L["orc"].forward(x, L["wr"], None, subset=sub)
+            check_routing(route, ref, T, cfg.E, cfg.k)
+            if outputs:
+                err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
+                worst = max(worst, float(err.max()))
+                assert err.max() <= REL_TOL, (s, l, err.max())
+        _say(f"stack step {s}: routing exact on all {cfg.layers} layers, worst rel err so far {worst:.3e}")
+    torch.cuda.synchronize()
+    for L in layers:
+        assert L["lay"].status() == 0
+
+
 # ----------------------------------------------------------------------------- edge cases
 SMALL = synth.MoEConfig("gsmall", 92, d=256, E=6, F=384, k=3, T=40, Fs=512,
                         bits_rule="uniform", bits_values=(1, 2, 3, 4, 5, 6, 7, 8))
