@@ -130,6 +130,24 @@ pw_status validate_tables(const pw_layer_s* L) {
     return PW_OK;
 }
 
+// Frees every device and pinned resource of the layer and clears the pointers,
+// so that a failed set-up leaves nothing behind and a later forward retries
+// from scratch. The caller has selected the layer's device.
+void release_device(pw_layer_s* L) {
+    for (int i = 0; i < kStageSlots; ++i) {
+        if (L->stage_ev[i]) (void)hipEventDestroy(L->stage_ev[i]);
+        if (L->h_stage[i]) (void)hipHostFree(L->h_stage[i]);
+        L->stage_ev[i] = nullptr;
+        L->h_stage[i] = nullptr;
+        L->stage_used[i] = false;
+    }
+    if (L->d_ws) (void)hipFree(L->d_ws);
+    if (L->d_blocks) (void)hipFree(L->d_blocks);
+    L->d_ws = nullptr;
+    L->d_blocks = nullptr;
+    L->dev_ready = false;
+}
+
 pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     if (L->dev_ready) return PW_OK;
     const pw_moe_desc& D = L->desc;
@@ -164,9 +182,8 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         return fail(PW_E_NOMEM, "workspace (%zu bytes): %s", off, hipGetErrorString(e));
     }
     if ((e = hipMalloc((void**)&L->d_blocks, sizeof(DevBlock) * n_blocks(L))) != hipSuccess) {
-        (void)hipFree(L->d_ws);
-        L->d_ws = nullptr;
         L->d_blocks = nullptr;
+        release_device(L);
         return fail(PW_E_NOMEM, "page table: %s", hipGetErrorString(e));
     }
     char* b = L->d_ws;
@@ -190,13 +207,19 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
             hipSuccess) {
             L->h_stage[i] = nullptr;
+            release_device(L);
             return fail(PW_E_NOMEM, "pinned staging: %s", hipGetErrorString(e));
         }
-        if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess)
+        if ((e = hipEventCreateWithFlags(&L->stage_ev[i], hipEventDisableTiming)) != hipSuccess) {
+            L->stage_ev[i] = nullptr;
+            release_device(L);
             return hip_fail(e, "hipEventCreate");
+        }
     }
-    if ((e = pw::launch_init_ws(L->ws, n_counters, L->wait_limit, s)) != hipSuccess)
+    if ((e = pw::launch_init_ws(L->ws, n_counters, L->wait_limit, s)) != hipSuccess) {
+        release_device(L);
         return hip_fail(e, "init workspace");
+    }
     L->dev_ready = true;
     return PW_OK;
 }
@@ -313,12 +336,7 @@ pw_status pw_layer_destroy(pw_layer L) {
     if (!L) return PW_OK;
     if (L->dev_ready || L->d_ws || L->d_blocks) {
         DeviceGuard g(L->device);
-        for (int i = 0; i < kStageSlots; ++i) {
-            if (L->stage_ev[i]) (void)hipEventDestroy(L->stage_ev[i]);
-            if (L->h_stage[i]) (void)hipHostFree(L->h_stage[i]);
-        }
-        if (L->d_ws) (void)hipFree(L->d_ws);
-        if (L->d_blocks) (void)hipFree(L->d_blocks);
+        release_device(L);
     }
     delete L;
     return PW_OK;
