@@ -14,7 +14,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpw.so")
 
-PW_ABI_VERSION = 1
+PW_ABI_VERSION = 2
+PW_FLAG_LUT_TILED = 1
 PW_GATE, PW_UP, PW_DOWN = 0, 1, 2
 PW_STATUS_ROUTER_RANGE = 1
 PW_STATUS_DEP_TIMEOUT = 2
@@ -68,7 +69,7 @@ def _load():
         "pw_moe_replay": ([P, i32, P], st),
         "pw_layer_last_bytes": ([P, P, ctypes.POINTER(ctypes.c_double)], st),
         "pw_debug_unpack": ([P, i32, i32, i32, P, P], st),
-        "pw_debug_dequant": ([P, i32, P, i32, i32, P, P], st),
+        "pw_debug_dequant": ([P, i32, P, u32, i32, i32, P, P], st),
         "pw_debug_set_wait_limit": ([P, u32], st),
     }
     for name, (args, res) in sig.items():
@@ -144,9 +145,10 @@ def pw_debug_unpack(planes, b: int, R: int, K: int, idx_out: int, stream: int = 
     _check(lib.pw_debug_unpack(arr, b, R, K, idx_out, stream or None))
 
 
-def pw_debug_dequant(planes, b: int, lut: int, R: int, K: int, w_out: int, stream: int = 0) -> None:
+def pw_debug_dequant(planes, b: int, lut: int, R: int, K: int, w_out: int, stream: int = 0,
+                     lut_flags: int = 0) -> None:
     arr = (ctypes.c_void_p * 8)(*([int(p) for p in planes] + [None] * (8 - len(planes))))
-    _check(lib.pw_debug_dequant(arr, b, lut, R, K, w_out, stream or None))
+    _check(lib.pw_debug_dequant(arr, b, lut, lut_flags, R, K, w_out, stream or None))
 
 
 def pw_debug_set_wait_limit(layer: int, polls: int) -> None:

@@ -300,7 +300,7 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     const pw_moe_desc& D = *desc;
     if (D.abi_version != PW_ABI_VERSION)
         return fail(PW_E_ARG, "abi_version %d, library is %d", D.abi_version, PW_ABI_VERSION);
-    if (D.flags != 0) return fail(PW_E_ARG, "flags must be 0");
+    if (D.flags & ~PW_FLAG_LUT_TILED) return fail(PW_E_ARG, "flags 0x%x: only PW_FLAG_LUT_TILED is defined", D.flags);
     if (D.d_model <= 0 || D.d_model % 128 || D.d_model > pw::kMaxModel)
         return fail(PW_E_SHAPE, "d_model %d: must be a positive multiple of 128, at most %d", D.d_model,
                     pw::kMaxModel);
@@ -404,6 +404,11 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     DeviceGuard guard(L->device);
     if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
     hipStream_t s = (hipStream_t)stream;
+    // every launch precondition (kernel attributes, occupancy) before the first enqueue
+    {
+        const hipError_t e = pw::prepare_experts();
+        if (e != hipSuccess) return hip_fail(e, "expert kernel set-up");
+    }
     if ((st = ensure_device(L, s)) != PW_OK) return st;
     if ((st = upload_tables(L, s)) != PW_OK) return st;
 
@@ -447,6 +452,7 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     gp.ws = L->ws;
     gp.ld_act = L->f_max;
     gp.shared_base = D.max_tokens * k;
+    gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
     gp.y = y;
     // gate_up + SwiGLU: items of 32 rows of F (gate and up)
     L->gp_gu = gp;
@@ -466,8 +472,12 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     L->res_y = y;
     L->res_out = (uint16_t*)x_next;
 
-    for (int phase = 0; phase < 3; ++phase)
-        if ((st = launch_phase(L, phase, s)) != PW_OK) return st;
+    for (int phase = 0; phase < 3; ++phase) {
+        if ((st = launch_phase(L, phase, s)) != PW_OK) {
+            L->dirty = true;   // the runtime refused a launch: upload the tables again next time
+            return st;
+        }
+    }
     static const bool debug_sync = getenv("PW_DEBUG_SYNC") != nullptr;   // read once per process
     if (debug_sync) {
         hipError_t e = hipStreamSynchronize(s);
@@ -555,14 +565,15 @@ pw_status pw_debug_unpack(const void* const* planes, int32_t b, int32_t R, int32
         if (!planes[p] || !aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d null or misaligned", p);
         p8[p + 8 - b] = (uint64_t)(uintptr_t)planes[p];
     }
-    hipError_t e = pw::launch_debug(p8, b, nullptr, R, K, idx_out, nullptr, (hipStream_t)stream);
+    hipError_t e = pw::launch_debug(p8, b, nullptr, 0, R, K, idx_out, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? PW_OK : hip_fail(e, "debug kernel");
 }
 
-pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut, int32_t R, int32_t K,
-                           void* w_out, void* stream) {
+pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut, uint32_t lut_flags, int32_t R,
+                           int32_t K, void* w_out, void* stream) {
     g_err.clear();
     if (!planes || !lut || !w_out) return fail(PW_E_ARG, "pw_debug_dequant: null argument");
+    if (lut_flags & ~PW_FLAG_LUT_TILED) return fail(PW_E_ARG, "lut_flags 0x%x", lut_flags);
     if (b < 1 || b > 8) return fail(PW_E_BITS, "b=%d not in 1..8", b);
     if (R <= 0 || R % 32 || K <= 0 || K % 128) return fail(PW_E_SHAPE, "R %% 32 and K %% 128 must be 0");
     if (!aligned16(lut) || !aligned16(w_out)) return fail(PW_E_ALIGN, "lut / w_out misaligned");
@@ -571,8 +582,8 @@ pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut
         if (!planes[p] || !aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d null or misaligned", p);
         p8[p + 8 - b] = (uint64_t)(uintptr_t)planes[p];
     }
-    hipError_t e = pw::launch_debug(p8, b, (const uint16_t*)lut, R, K, nullptr, (uint16_t*)w_out,
-                                    (hipStream_t)stream);
+    hipError_t e = pw::launch_debug(p8, b, (const uint16_t*)lut, (lut_flags & PW_FLAG_LUT_TILED) ? 1 : 0, R, K,
+                                    nullptr, (uint16_t*)w_out, (hipStream_t)stream);
     return e == hipSuccess ? PW_OK : hip_fail(e, "debug kernel");
 }
 

@@ -83,6 +83,7 @@ struct GemmParams {
     Workspace ws;
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
+    int lut_tiled;            // LUT pages in the 32-row tiled order (else row-major)
     const uint16_t* x;        // layer input (gate_up B operand)
     uint32_t b_bytes;         // size of the B-operand buffer (x or act)
     float* y;
@@ -101,9 +102,13 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
 // The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s);
+// Sets the expert kernels' attributes and caches their per-CU occupancy; the
+// forward calls it before enqueueing anything, so a launch precondition that
+// cannot be met fails the call with nothing enqueued.
+hipError_t prepare_experts();
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
                            hipStream_t s);
-hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
+hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int lut_tiled, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
 // LDS bytes of the expert kernel for items of tile_tokens tokens.
@@ -113,6 +118,8 @@ constexpr int kSmallTokens = 16;          // token group of the one-tile kernel 
 constexpr int kSmallMax = 32;             // experts with 1..32 tokens: groups of 16 in the one-tile kernel
 constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
+// act rows of one K-piece start on a 128-byte line (2-byte elements): a line never holds two pieces
+static_assert(kDownPiece % 64 == 0, "K-pieces must start on 128-byte act lines");
 constexpr int kRouteThreads = 256;          // route kernel: 4 waves
 constexpr int kRouteExpertsPerWave = 2;     // router rows per wave
 constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)

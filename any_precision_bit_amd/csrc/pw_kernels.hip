@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdlib>
 
 #include "pw.h"
 #include "pw_internal.h"
@@ -93,18 +94,25 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* kconst(con
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 
+// Exact product of two fp16 values in units of 2^-48, added to acc. A finite
+// fp16 magnitude is mant * 2^(sh - 24) with mant < 2^11 and sh = max(e, 1) - 1
+// (e the biased exponent field; mant carries the implicit bit when e > 0), so
+// |x w| * 2^48 = (mant_x * mant_w) << (sh_x + sh_w): a 22-bit integer product
+// shifted left, exact whenever |x w| < 2^15. sab accumulates |x w| in fp32 for
+// the range check; inf / nan operands set bad.
 __device__ __forceinline__ void add_pair(uint32_t xw, uint32_t ww, long long& acc, float& sab,
                                          int& bad) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const float xf = h2f((uint16_t)(xw >> (16 * h)));
-        const float wf = h2f((uint16_t)(ww >> (16 * h)));
-        bad |= !(fabsf(xf) < 128.0f) | !(fabsf(wf) < 128.0f);
-        // exact: |x|,|w| < 128, so x*2^24 and w*2^24 are integers below 2^31
-        const int X = (int)(xf * 16777216.0f);
-        const int W = (int)(wf * 16777216.0f);
-        acc += (long long)X * (long long)W;
-        sab = fmaf(fabsf(xf), fabsf(wf), sab);
+        const uint32_t hx = (xw >> (16 * h)) & 0xFFFFu, hw = (ww >> (16 * h)) & 0xFFFFu;
+        const uint32_t ex = (hx >> 10) & 31u, ew = (hw >> 10) & 31u;
+        bad |= (ex == 31u) | (ew == 31u);
+        const uint32_t mx = (hx & 1023u) | (ex ? 1024u : 0u);
+        const uint32_t mw = (hw & 1023u) | (ew ? 1024u : 0u);
+        const uint32_t sh = (ex ? ex - 1u : 0u) + (ew ? ew - 1u : 0u);   // 0..60
+        const long long prod = (long long)((unsigned long long)(mx * mw) << sh);
+        acc += ((hx ^ hw) & 0x8000u) ? -prod : prod;
+        sab = fmaf(fabsf(h2f((uint16_t)hx)), fabsf(h2f((uint16_t)hw)), sab);
     }
 }
 
@@ -342,8 +350,10 @@ __device__ __forceinline__ void exact_logits(const RouteParams& p, int t, int e0
 // Routing and bucket sort in one launch of T * ceil(E / (4 * kRouteExpertsPerWave))
 // work-groups of 4 waves. Work-group (t, eb) computes the exact logits (int64,
 // units of 2^-48) of its experts for token t, kRouteExpertsPerWave per wave:
-// with |x|, |w| < 128, x*2^24 and w*2^24 are integers below 2^31 and their
-// products are exact. The work-group that finishes token t last (a counter per
+// every product is an exponent-aligned integer mantissa product (add_pair), and
+// the sum is exact for any finite fp16 inputs with sum |x w| + |bias| < 2^15
+// (checked in fp32 with margin; outside it a status flag is raised). The
+// work-group that finishes token t last (a counter per
 // token) ranks all E exact logits (ties to the lower expert index), keeps the
 // top k and takes the softmax over them; the one that finishes the last token
 // does the bucket sort and the work lists. Values passed between work-groups
@@ -533,33 +543,42 @@ __device__ __forceinline__ void write_stripe8(uint32_t* stripe, int c8, int row,
     }
 }
 
-// LUT pages are stored in 32-row tiles: a tile holds, for entry group g =
-// 0 .. max(1, 2^b/8) - 1, the entries [8g, 8g + min(8, 2^b)) of its 32 rows, row
-// after row. The tile of an item's 32 rows of one row-set is 32 * 2^b contiguous
-// fp16 values, staged with coalesced 16-byte loads: thread t takes units t,
-// t + 256, ... (4 * 2^b units per set, at most 4 per thread at b = 8). For
-// b >= 3 unit u is entries 8*(u >> 5) .. +7 of row u & 31. The loads are issued
-// early (lut_stage_load) and written to the stripe later (lut_stage_write).
+// The LUTs of an item's 32 rows of one row-set are 32 * 2^b contiguous fp16
+// values in either page order: row-major (entry i of row r at r * 2^b + i) or,
+// with PW_FLAG_LUT_TILED, the 32-row tiled order (entry group g = i / 8 of the
+// 32 rows row after row: entry i of row r at (g * 32 + r) * 8 + i % 8). They are
+// staged in 16-byte units of 8 entries: thread t takes row t & 31 and entry
+// groups g = (t >> 5) + 8 * it, it = 0..3 (4 * 2^b units per set, at most 4 per
+// thread at b = 8), so each half-wave covers rows 0..31 and the stripe writes
+// hit 32 distinct banks. In the tiled order a wave's loads are contiguous; in
+// the row-major order they are 16 bytes per row at a 2^b * 2-byte stride. For
+// b < 3 a row is shorter than a unit and both orders are the same row-major
+// array (unit u is bytes 16u .. 16u + 15 of it). The loads are issued early
+// (lut_stage_load) and written to the stripe later (lut_stage_write).
 struct LutStage {
     uint4 v[2][4];
 };
+__device__ __forceinline__ uint32_t lut_unit_offset(int u, int b, int tiled) {
+    if (b < 3 || tiled) return (uint32_t)u * 8u;              // element offset of unit u
+    return (uint32_t)(((u & 31) << (b - 3)) + (u >> 5)) * 8u;   // row (u & 31), group u >> 5
+}
 __device__ __forceinline__ void lut_stage_load(LutStage& st, const uint16_t* lut0, int b0,
-                                               const uint16_t* lut1, int b1, int tid) {
+                                               const uint16_t* lut1, int b1, int tid, int tiled) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int u = tid + it * 256;
-        st.v[0][it] = u < (4 << b0) ? *(const uint4*)(lut0 + 8 * u) : make_uint4(0, 0, 0, 0);
-        st.v[1][it] = u < (4 << b1) ? *(const uint4*)(lut1 + 8 * u) : make_uint4(0, 0, 0, 0);
+        st.v[0][it] = u < (4 << b0) ? *(const uint4*)(lut0 + lut_unit_offset(u, b0, tiled)) : make_uint4(0, 0, 0, 0);
+        st.v[1][it] = u < (4 << b1) ? *(const uint4*)(lut1 + lut_unit_offset(u, b1, tiled)) : make_uint4(0, 0, 0, 0);
     }
 }
 
-// Debug-kernel stripe (dword idx*64 + row, both halves the same) from one
-// 32-row LUT tile, one wave, plain loop.
-__device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* tile, int b, int lane) {
+// Debug-kernel stripe (dword idx*64 + row, both halves the same) from the LUTs
+// of 32 rows (row-major, or 32-row tiled), one wave, plain loop.
+__device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* tile, int b, int tiled, int lane) {
     const int nidx = 1 << b;
     for (int e = lane; e < 32 * nidx; e += 64) {
         int row, idx;
-        if (b >= 3) {
+        if (b >= 3 && tiled) {
             row = (e >> 3) & 31;
             idx = ((e >> 8) << 3) | (e & 7);
         } else {
@@ -745,9 +764,21 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 //
 // Gate_up items come first in the combined order (index i < n_gu), down items
 // after them. A down item reads the act rows of its expert's K-piece, so it
-// waits until every gate_up item of that (list position, piece) has released
-// its act stores (agent-scope release, then a counter increment; the down item
-// spins on the counter and then acquires). Every dependency points to an
+// waits until every gate_up item of that (list position, piece) has counted
+// itself done. There is no fence on either side; the hand-off rests on these
+// invariants:
+//   - act is written only with device-coherent (agent-scope, sc1) stores, which
+//     write through to memory; each producer wave drains them (vmcnt 0) before
+//     the work-group barrier after which thread 0 increments the counter;
+//   - the consumer polls the counter with device-coherent loads and issues no
+//     load of act (nor of any line holding act) before its wait ends, so no
+//     cache level can hold a stale copy of a piece's act lines: they were last
+//     touched by the previous launch, and a kernel boundary writes back and
+//     invalidates the non-coherent caches;
+//   - K-pieces (kDownPiece columns) and act rows start on 128-byte lines, so a
+//     line never mixes act of two pieces.
+// A change that loads B rows of a down item before its wait (say, in the
+// next-item prefetch) breaks the second invariant. Every dependency points to an
 // earlier index of the combined order and each work-group runs its items in
 // increasing order, so with all work-groups resident (the launch sizes the grid
 // to the occupancy) the earliest unfinished item never waits: no deadlock. The
@@ -818,7 +849,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
         auto lut_load = [&](const Item& it, LutStage& st) {
             const int b0 = it.blk0->bits, b1 = it.blk1->bits;
             lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
-                           (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid);
+                           (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid, g.lut_tiled);
         };
         auto publish_item = [&](const Item& it, const LutStage& st, const TokInfo& tk, int par) {
             if (tid < it.nl) {
@@ -949,6 +980,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             // as pa has been consumed for the last time.
             LutStage st;
             bool fetched = false;
+            // The next item's planes, LUT rows and token rows only: never its B rows,
+            // which for a down item may only be read after its dependency wait.
             auto fetch_next = [&]() {
                 if (has_next) {
                     load_chunk(nit, 0, pa0, pa1);
@@ -1084,6 +1117,7 @@ struct DebugParams {
     uint64_t planes[8];
     const uint16_t* lut;
     int b, R, K;
+    int lut_tiled;
     uint8_t* idx_out;
     uint16_t* w_out;
 };
@@ -1097,7 +1131,7 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
     const int Kb = p.K >> 3;
     if (p.w_out) {
         const uint16_t* lut = p.lut + ((size_t)rb << p.b);
-        stage_lut32((uint32_t*)smem, lut, p.b, lane);
+        stage_lut32((uint32_t*)smem, lut, p.b, p.lut_tiled, lane);
     }
     __syncthreads();
     const uint32_t slot = lds_addr(smem) + (uint32_t)(r * 4);
@@ -1175,6 +1209,18 @@ static hipError_t expert_occupancy(int* per_cu) {
     return hipSuccess;
 }
 
+// PW_COOPERATIVE=1 (read once per process) launches the expert kernels
+// cooperatively: the runtime then guarantees that every work-group is resident
+// at once, or fails the launch, instead of the grid being sized to the
+// occupancy and trusted to fit.
+static bool cooperative_launch() {
+    static const bool on = [] {
+        const char* v = getenv("PW_COOPERATIVE");
+        return v != nullptr && v[0] == '1';
+    }();
+    return on;
+}
+
 template <int NT>
 static hipError_t launch_experts_t(const ExpertParams& p, int n_cu, hipStream_t s) {
     int per_cu = 0;
@@ -1182,8 +1228,22 @@ static hipError_t launch_experts_t(const ExpertParams& p, int n_cu, hipStream_t 
     if (err != hipSuccess) return err;
     if (per_cu < 1) return hipErrorLaunchOutOfResources;
     // every work-group resident at once: the dependency waits rely on it
+    if (cooperative_launch()) {
+        ExpertParams arg = p;
+        void* args[] = {(void*)&arg};
+        return hipLaunchCooperativeKernel((const void*)expert_kernel<NT>, dim3(per_cu * n_cu), dim3(256), args,
+                                          (unsigned)expert_lds_bytes(16 * NT), s);
+    }
     hipLaunchKernelGGL((expert_kernel<NT>), dim3(per_cu * n_cu), dim3(256), expert_lds_bytes(16 * NT), s, p);
     return hipGetLastError();
+}
+
+hipError_t prepare_experts() {
+    int a = 0, b = 0;
+    hipError_t err = expert_occupancy<1>(&a);
+    if (err == hipSuccess) err = expert_occupancy<4>(&b);
+    if (err != hipSuccess) return err;
+    return (a < 1 || b < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
 }
 
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {
@@ -1197,11 +1257,12 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, 
     return hipGetLastError();
 }
 
-hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int R, int K,
+hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int lut_tiled, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s) {
     DebugParams p;
     for (int q = 0; q < 8; ++q) p.planes[q] = planes8[q];
     p.lut = lut;
+    p.lut_tiled = lut_tiled;
     p.b = b;
     p.R = R;
     p.K = K;

@@ -1,9 +1,10 @@
 """Page formats of the library (host-side data preparation; no layer compute).
 
 Bit-plane pages are row-major (row stride K/8 bytes, column c at bit c & 7 of
-byte c >> 3). LUT pages are stored in 32-row tiles so that the kernels read a
-tile with coalesced loads: `lut_page` reorders a per-row table [R, 2^b] (fp16,
-R a multiple of 32) into that order. The byte size is unchanged.
+byte c >> 3). LUT pages are row-major per-row tables [R, 2^b] by default; a
+layer created with PW_FLAG_LUT_TILED takes them in 32-row tiles instead, which
+a work-group stages with contiguous loads: `lut_page` reorders a per-row table
+(fp16, R a multiple of 32) into that order. The byte size is unchanged.
 """
 from __future__ import annotations
 

@@ -13,9 +13,15 @@
  *     "Key Takeaways" and FAQ Q5)                           -> pw_moe_forward
  *
  * Conventions shared by every entry point
- *   - Every function returns pw_status; nothing throws across the ABI. On a
- *     non-OK status nothing is enqueued on any stream and the layer's state is
- *     unchanged; pw_last_error() (thread-local) then describes the failure.
+ *   - Every function returns pw_status; nothing throws across the ABI. Every
+ *     argument, shape and launch precondition is checked before anything is
+ *     enqueued: on a non-OK status from a check nothing is enqueued on any
+ *     stream and the layer's state is unchanged. The one exception is
+ *     PW_E_HIP from pw_moe_forward when the HIP runtime rejects a kernel
+ *     launch itself (after the checks passed): kernels enqueued before the
+ *     failing launch stay enqueued, y is then undefined, and the device
+ *     tables are uploaded again by the next forward. pw_last_error()
+ *     (thread-local) describes every failure.
  *   - "device pointer" means memory of the GPU the layer runs on. The caller
  *     owns every device buffer (pages, LUTs, x, y, router weights, route
  *     outputs); the library owns only the handle, its device tables and its
@@ -31,9 +37,15 @@
  *     of a row is bit (c & 7) of byte (c >> 3).
  *   - at bitwidth b the weight is LUT_b[r][q >> (8-b)], read from planes 0..b-1;
  *     LUT_b has one table of 2^b fp16 entries per output row r (R * 2^b values),
- *     stored in 32-row tiles: with E = min(8, 2^b) and G = 2^b / E, entry i of
- *     row r sits at element ((t*G + g)*32 + rr)*E + j, where t = r / 32,
- *     rr = r % 32, g = i / E, j = i % E (R must be a multiple of 32).
+ *     row-major: entry i of row r at element r * 2^b + i.
+ *   - alternative LUT page order, selected per layer with PW_FLAG_LUT_TILED in
+ *     pw_moe_desc.flags: 32-row tiles; with E = min(8, 2^b) and G = 2^b / E,
+ *     entry i of row r sits at element ((t*G + g)*32 + rr)*E + j, where
+ *     t = r / 32, rr = r % 32, g = i / E, j = i % E. It holds the same values in
+ *     the same bytes; a work-group then stages a tile's tables with contiguous
+ *     loads. (For b < 3 both orders are the same array.)
+ *   - R (every block's row count: d_model and the ffn sizes) is a multiple of
+ *     32 and K a multiple of 128, which the size limits below imply.
  */
 #ifndef PW_H
 #define PW_H
@@ -44,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PW_ABI_VERSION 1
+#define PW_ABI_VERSION 2
 #define PW_MAX_BITS 8
 #define PW_MAX_TOP_K 16
 #define PW_MAX_EXPERTS 256
@@ -82,8 +94,11 @@ typedef struct {
                               the shared expert has expert id E */
     int32_t max_tokens;    /* upper bound on T per forward, 1..65536, with
                               max_tokens*(top_k+1)*max(d_ffn, d_ffn_shared) < 2^31 */
-    uint32_t flags;        /* must be 0 */
+    uint32_t flags;        /* 0, or PW_FLAG_LUT_TILED: every bound LUT page of this layer
+                              is in the 32-row tiled order (default: row-major) */
 } pw_moe_desc;
+
+#define PW_FLAG_LUT_TILED 1u
 
 /* Optional routing outputs of a forward, all device pointers; any may be NULL.
  * topk_ids int32 [T][k] (descending logit, ties to the lower expert index),
@@ -119,7 +134,7 @@ pw_status pw_moe_plan_set(pw_layer layer, const uint8_t* bits, int32_t n_blocks)
 /* Binds the pages of block (expert, linear): planes[p] for p < n_planes are
  * device pointers to bit-plane p (planes 0..n_planes-1 of the parent, 16-byte
  * aligned, R*K/8 bytes each); lut is a device pointer to LUT_{lut_bits}
- * (R * 2^lut_bits fp16 in the tiled order above, 16-byte aligned). The host
+ * (R * 2^lut_bits fp16 in the layer's LUT page order above, 16-byte aligned). The host
  * array `planes` is copied before return. The pages must stay alive until every forward enqueued while
  * they were bound has completed on its stream. A forward requires, for every
  * block, n_planes >= b and lut_bits == b for the planned b (else PW_E_UNBOUND). */
@@ -133,13 +148,19 @@ pw_status pw_page_table_bind(pw_layer layer, int32_t expert, int32_t linear,
  *   router_w fp16 [E][d] device, 16-byte aligned
  *   router_b fp16 [E] device or NULL (added to the logits)
  *   y        fp32 [T][d] device, overwritten with
- *            sum_j w_j * expert_{ids_j}(x_t) (+ shared expert(x_t))
+ *            sum_j w_j * expert_{ids_j}(x_t) (+ shared expert(x_t)); each expert
+ *            accumulates in fp32 and rounds its SwiGLU output silu(g) * u to
+ *            fp16 (the down projection's matrix-core operand), so outputs are
+ *            defined while |silu(g) * u| <= 65504
  *   x_next   fp16 [T][d] device or NULL: fp16 round-to-nearest-even of x + y
  *   route    optional routing outputs (NULL = none)
  * Routing is exact: logits are compared as exact integers in units of 2^-48.
- * That needs |x|, |router_w| < 128 and sum_c |x*w| + |b| < 2^15 per (token,
- * expert); a token/expert outside that range sets PW_STATUS_ROUTER_RANGE in the
- * device status word (read with pw_layer_status) and its routing is undefined.
+ * Every finite fp16 x, router_w and router_b is accepted; the sum is exact
+ * when sum_c |x*w| + |b| < 2^15 per (token, expert) (checked on the device in
+ * fp32 with a 2 % margin). A token/expert outside that range, or a non-finite
+ * input, sets PW_STATUS_ROUTER_RANGE in the device status word (read with
+ * pw_layer_status) and its routing is undefined. The check needs the inputs,
+ * which live on the device, so it cannot fail the call itself.
  * T == 0 is a no-op. With the environment variable PW_DEBUG_SYNC set (read once
  * per process) the call synchronises `stream` before returning, so that a
  * kernel fault surfaces here as PW_E_HIP. */
@@ -169,13 +190,13 @@ pw_status pw_layer_last_bytes(pw_layer layer, void* stream, double* bytes /*[4]*
 
 /* Test hooks for one block, same kernels' dequantisation path as the forward:
  * indices u8 [R][K] of bitwidth b (pw_debug_unpack) and weights fp16 [R][K]
- * (pw_debug_dequant, lut in the tiled order above), for an [R x K] block with
- * R % 32 == 0 and K % 128 == 0.
+ * (pw_debug_dequant; lut row-major, or 32-row tiled when lut_flags has
+ * PW_FLAG_LUT_TILED), for an [R x K] block with R % 32 == 0 and K % 128 == 0.
  * All pointers are device pointers; the call is asynchronous on `stream`. */
 pw_status pw_debug_unpack(const void* const* planes, int32_t b, int32_t R, int32_t K,
                           uint8_t* idx_out, void* stream);
-pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut, int32_t R,
-                           int32_t K, void* w_out, void* stream);
+pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut, uint32_t lut_flags,
+                           int32_t R, int32_t K, void* w_out, void* stream);
 
 /* Test hook: how many times a down item polls the counter of its gate_up rows
  * before it gives up, sets PW_STATUS_DEP_TIMEOUT and goes on (later forwards of
