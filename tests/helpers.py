@@ -18,19 +18,21 @@ def rel_err_per_token(y, ref):
     return num / np.maximum(den, 1e-30)
 
 
-def device_pages(blocks, bits, device, all_luts=False):
+def device_pages(blocks, bits, device, all_luts=False, lut_tiled=False):
     """Copies each block's planes 0..b-1 (all generated planes when all_luts)
-    and its LUT(s), in the tiled LUT page order, to the device. Returns {(e, lin): (planes u8 [n,R,K/8], {b: lut fp16})}."""
+    and its LUT(s), row-major (or in the 32-row tiled page order), to the device.
+    Returns {(e, lin): (planes u8 [n,R,K/8], {b: lut fp16})}."""
     import torch
     from any_precision_bit_amd.pages import lut_page
 
+    order = lut_page if lut_tiled else np.ascontiguousarray
     out = {}
     for (e, lin), blk in blocks.items():
         b = int(bits[e, lin])
         n = blk.planes.shape[0] if all_luts else b
         planes = torch.from_numpy(np.ascontiguousarray(blk.planes[:n])).to(device)
         lb = blk.luts.keys() if all_luts else [b]
-        luts = {int(bb): torch.from_numpy(lut_page(blk.luts[bb]).view(np.int16).copy()).to(device)
+        luts = {int(bb): torch.from_numpy(order(blk.luts[bb]).view(np.int16).copy()).to(device)
                 .view(torch.float16) for bb in lb}
         out[(e, lin)] = (planes, luts)
     return out
@@ -42,10 +44,10 @@ def bind_all(layer, bits, pages):
         layer.bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
 
 
-def gpu_layer(cfg, bits, pages, max_tokens=None):
+def gpu_layer(cfg, bits, pages, max_tokens=None, lut_tiled=False):
     from any_precision_bit_amd import PagedMoELayer
 
-    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, max_tokens or max(cfg.T, 1))
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, max_tokens or max(cfg.T, 1), lut_tiled=lut_tiled)
     lay.plan_set(bits)
     bind_all(lay, bits, pages)
     return lay

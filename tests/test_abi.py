@@ -45,9 +45,11 @@ def test_create_validation(B):
     with pytest.raises(B.PwError) as ei:
         B.pw_layer_create(**ok, abi_version=99)
     assert ei.value.status == 1
-    with pytest.raises(B.PwError) as ei:
-        B.pw_layer_create(**ok, flags=1)
-    assert ei.value.status == 1
+    B.pw_layer_destroy(B.pw_layer_create(**ok, flags=B.PW_FLAG_LUT_TILED))   # the one defined flag
+    for bad_flags in (2, 0x80000000):
+        with pytest.raises(B.PwError) as ei:
+            B.pw_layer_create(**ok, flags=bad_flags)
+        assert ei.value.status == 1
     B.pw_layer_destroy(None)   # no-op
 
 
@@ -139,6 +141,9 @@ def test_debug_hook_validation(B):
     with pytest.raises(B.PwError) as ei:
         B.pw_debug_dequant(p, 3, (1 << 40) + 2, 32, 128, 1 << 41)
     assert ei.value.status == 5
+    with pytest.raises(B.PwError) as ei:
+        B.pw_debug_dequant(p, 3, 1 << 40, 32, 128, 1 << 41, lut_flags=2)
+    assert ei.value.status == 1
 
 
 def test_status_and_replay_without_device_state(B):

@@ -43,12 +43,14 @@ def test_unpack_and_dequant_bit_exact(torch_dev, R, K):
         ref_idx = oracle.unpack_indices(planes_h, b)
         assert np.array_equal(idx.cpu().numpy(), ref_idx), b
         lut_h = (rng.standard_normal((R, 1 << b)) * 0.02).astype(np.float16)
-        lut = to_dev_f16(lut_page(lut_h), dev)
-        w = torch.zeros((R, K), dtype=torch.float16, device=dev)
-        B.pw_debug_dequant([planes[p].data_ptr() for p in range(b)], b, lut.data_ptr(), R, K, w.data_ptr())
-        torch.cuda.synchronize()
         ref_w = oracle.dequant(planes_h, b, lut_h).astype(np.float16)
-        assert np.array_equal(f16_host(w).view(np.uint16), ref_w.view(np.uint16)), b
+        for tiled in (False, True):
+            lut = to_dev_f16(lut_page(lut_h) if tiled else lut_h, dev)
+            w = torch.zeros((R, K), dtype=torch.float16, device=dev)
+            B.pw_debug_dequant([planes[p].data_ptr() for p in range(b)], b, lut.data_ptr(), R, K, w.data_ptr(),
+                               lut_flags=B.PW_FLAG_LUT_TILED if tiled else 0)
+            torch.cuda.synchronize()
+            assert np.array_equal(f16_host(w).view(np.uint16), ref_w.view(np.uint16)), (b, tiled)
 
 
 # ----------------------------------------------------------------------------- layer parity
@@ -63,13 +65,14 @@ def check_routing(route, ref, T, E, k):
     assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -23 + 1e-6)
 
 
-def run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=None, pages=None):
+def run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=None, pages=None, lut_tiled=False,
+               max_tokens=None):
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
     T = x.shape[0]
-    pages = pages or device_pages(blocks, bits, dev)
-    lay = layer or gpu_layer(cfg, bits, pages, max_tokens=T)
+    pages = pages or device_pages(blocks, bits, dev, lut_tiled=lut_tiled)
+    lay = layer or gpu_layer(cfg, bits, pages, max_tokens=max_tokens or T, lut_tiled=lut_tiled)
     xd, wd = to_dev_f16(x, dev), to_dev_f16(wr, dev)
     bd = None if bias is None else to_dev_f16(bias, dev)
     route = route_buffers(T, cfg.E, cfg.k, dev)
@@ -98,13 +101,14 @@ def test_tiny_full(torch_dev):
     run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
 
 
-def test_qwen_decode_full(torch_dev):
+@pytest.mark.parametrize("lut_tiled", [False, True])
+def test_qwen_decode_full(torch_dev, lut_tiled):
     cfg = synth.CONFIGS["qwen_d2048_t16"]
-    _say("qwen_d2048_t16")
+    _say(f"qwen_d2048_t16 lut_tiled={lut_tiled}")
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     x, wr, bias = layer_inputs(cfg)
-    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
+    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), lut_tiled=lut_tiled)
 
 
 @pytest.fixture(scope="module")
@@ -114,13 +118,13 @@ def c2_data():
     return cfg, bits, _blocks(cfg, bits)
 
 
-@pytest.mark.parametrize("T,n_check", [(1, 1), (64, 8)])
-def test_mixtral(torch_dev, c2_data, T, n_check):
+@pytest.mark.parametrize("T", [1, 64])
+def test_mixtral(torch_dev, c2_data, T):
     cfg, bits, blocks = c2_data
     _say(f"mixtral_d4096 T={T}")
     cfgT = cfg.with_tokens(T)
     x, wr, bias = layer_inputs(cfgT)
-    run_parity(torch_dev, cfgT, bits, blocks, x, wr, bias, sample_tokens(T, n_check, seed=T))
+    run_parity(torch_dev, cfgT, bits, blocks, x, wr, bias, np.arange(T, dtype=np.int32))
 
 
 def test_fine_e128(torch_dev):
@@ -132,15 +136,31 @@ def test_fine_e128(torch_dev):
     counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
     bits = synth.initial_bits(cfg, counts=counts)
     blocks = _blocks(cfg, bits)
-    _, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, sample_tokens(cfg.T, 24, seed=3))
+    _, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
     assert ref["counts"].max() > 32          # exercises the multi-tile (large) kernels
 
 
+def _rewrite_all(cfg, layers, s):
+    """The plan rewrite before step s (a multiple of the rewrite period): each layer's seeded blocks
+    lose bits; the GPU layer is re-planned and the changed blocks rebound; the oracle follows."""
+    for l, L in enumerate(layers):
+        new, changed = synth.rewrite_plan(cfg, L["bits"], layer=l, epoch=s // cfg.rewrite_every)
+        L["bits"] = new
+        L["lay"].plan_set(new)
+        for blk in changed:
+            e, lin = divmod(int(blk), 3)
+            planes, luts = L["pages"][(e, lin)]
+            b = int(new[e, lin])
+            L["lay"].bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
+        L["orc"].set_bits(new)
+
+
 def test_qwen_stack_teacher_forced(torch_dev):
-    """A 3-layer slice of the 24-layer stack, 64 decode steps at T=256 with the
-    plan rewritten (and pages rebound) before steps 16, 32 and 48. Every step
-    runs on the GPU; routing is checked in full and outputs on 4 sampled tokens
-    at the steps around each rewrite, each layer on the GPU's own input."""
+    """A 3-layer slice of the 24-layer stack, 64 decode steps at T=256 with the plan rewritten (and
+    pages rebound) before steps 16, 32 and 48, each layer fed by the previous layer's residual output.
+    Every step of every layer is checked on the GPU's own input (teacher forcing): routing on all 256
+    tokens (ids, weights, counts, offsets, sorted order), the residual bit-exactly, and outputs on 2
+    seeded tokens (8 at the steps on both sides of a rewrite)."""
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
@@ -155,41 +175,34 @@ def test_qwen_stack_teacher_forced(torch_dev):
         wr, bias = synth.router(cfg, layer=l)
         layers.append(dict(bits=bits, blocks=blocks, pages=pages, lay=lay, wr=wr,
                            wd=to_dev_f16(wr, dev), orc=oracle.OracleLayer.from_config(cfg, bits, blocks)))
-    check_steps = {0, 15, 16, 31, 32, 47, 48, 63}
+    around = {0, 15, 16, 31, 32, 47, 48, 63}
     route = route_buffers(T, cfg.E, cfg.k, dev)
     y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
+    worst = 0.0
     for s in range(cfg.steps):
         if s > 0 and s % cfg.rewrite_every == 0:
-            for l, L in enumerate(layers):
-                new, changed = synth.rewrite_plan(cfg, L["bits"], layer=l, epoch=s // cfg.rewrite_every)
-                L["bits"] = new
-                L["lay"].plan_set(new)
-                for blk in changed:
-                    e, lin = divmod(blk, 3)
-                    planes, luts = L["pages"][(e, lin)]
-                    b = int(new[e, lin])
-                    L["lay"].bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
-                L["orc"].set_bits(new)
+            _rewrite_all(cfg, layers, s)
         x = to_dev_f16(synth.tokens(cfg, T, step=s), dev)
         for l, L in enumerate(layers):
             x_next = torch.empty_like(x)
             L["lay"].forward(x, L["wd"], None, y=y, x_next=x_next, route=route)
-            if s in check_steps:
-                torch.cuda.synchronize()
-                xh = f16_host(x)
-                sub = sample_tokens(T, 4, seed=100 * s + l)
-                ref = L["orc"].forward(xh, L["wr"], None, subset=sub)
-                check_routing(route, ref, T, cfg.E, cfg.k)
-                err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
-                _say(f"qwen_stack24_t256 step {s} layer {l}: max rel err {err.max():.3e}")
-                assert err.max() <= REL_TOL
-                xn_ref = oracle.residual(xh, y.cpu().numpy())   # O9 on the GPU's own y
-                assert np.array_equal(f16_host(x_next).view(np.uint16), xn_ref.view(np.uint16))
+            torch.cuda.synchronize()
+            xh = f16_host(x)
+            sub = sample_tokens(T, 8 if s in around else 2, seed=100 * s + l)
+            ref = L["orc"].forward(xh, L["wr"], None, subset=sub)
+            check_routing(route, ref, T, cfg.E, cfg.k)
+            yh = y.cpu().numpy()
+            err = rel_err_per_token(yh[sub], ref["y"][sub])
+            worst = max(worst, float(err.max()))
+            assert err.max() <= REL_TOL, (s, l, err.max())
+            xn_ref = oracle.residual(xh, yh)   # O9 on the GPU's own y
+            assert np.array_equal(f16_host(x_next).view(np.uint16), xn_ref.view(np.uint16)), (s, l)
             x = x_next
+        if s % 8 == 7:
+            _say(f"qwen_stack24_t256 3-layer slice: steps 0..{s} checked, worst rel err {worst:.3e}")
     torch.cuda.synchronize()
     for L in layers:
         assert L["lay"].status() == 0
-
 
 
 def test_dependency_wait_limit_flags_and_recovers(torch_dev):
@@ -221,19 +234,19 @@ def test_dependency_wait_limit_flags_and_recovers(torch_dev):
 
 
 def test_qwen_stack_all_layers_independent_inputs(torch_dev):
-    """All 24 layers of the stack at T=256, with the plan rewritten (and pages rebound) before steps
-    16, 32 and 48, in the configuration `bench.py --stack` times: each layer takes its own seeded
-    input per step. The steps on both sides of each rewrite run: routing is checked on every token
-    of every layer, and outputs on one sampled token of a quarter of the layers (rotating) at the
-    first step of each plan epoch. A forward leaves no state behind but the plan and the pages, so
-    the steps in between, which only repeat the same kernels, are skipped."""
+    """All 24 layers of the stack at T=256 over all 64 decode steps, with the plan rewritten (and pages
+    rebound) before steps 16, 32 and 48, in the configuration `bench.py` times: each layer takes its own
+    seeded input per step and writes its residual. Every (layer, step) runs on the GPU and its routing
+    is checked on every token (ids, weights, counts, offsets, sorted order). Outputs are checked on one
+    seeded token in three layers per step, rotating so that each layer is output-checked twice in every
+    plan epoch, and the residual of those layers bit-exactly."""
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
     from concurrent.futures import ThreadPoolExecutor
 
     cfg = synth.CONFIGS["qwen_stack24_t256"]
-    T = cfg.T
+    T, n_layers = cfg.T, cfg.layers
 
     def reachable(b):   # bitwidths a block at b passes through under the rewrites
         out = {b}
@@ -250,7 +263,7 @@ def test_qwen_stack_all_layers_independent_inputs(torch_dev):
         return {(blk.e, blk.lin): blk for blk in made}
 
     layers = []
-    for l in range(cfg.layers):
+    for l in range(n_layers):
         bits = synth.initial_bits(cfg, layer=l)
         blocks = stack_blocks(bits, l)
         pages = device_pages(blocks, bits, dev, all_luts=True)
@@ -258,40 +271,39 @@ def test_qwen_stack_all_layers_independent_inputs(torch_dev):
         wr, _ = synth.router(cfg, layer=l)
         layers.append(dict(bits=bits, pages=pages, lay=lay, wr=wr, wd=to_dev_f16(wr, dev),
                            orc=oracle.OracleLayer.from_config(cfg, bits, blocks)))
-    _say(f"stack: {cfg.layers} layers ready")
-    check_steps = {0, 15, 16, 31, 32, 47, 48, 63}
+    _say(f"stack: {n_layers} layers ready")
     route = route_buffers(T, cfg.E, cfg.k, dev)
     y = torch.empty((T, cfg.d), dtype=torch.float32, device=dev)
     x_next = torch.empty((T, cfg.d), dtype=torch.float16, device=dev)
+    per_step = 3
+    seen = set()
     worst = 0.0
     for s in range(cfg.steps):
         if s > 0 and s % cfg.rewrite_every == 0:
-            for l, L in enumerate(layers):
-                new, changed = synth.rewrite_plan(cfg, L["bits"], layer=l, epoch=s // cfg.rewrite_every)
-                L["bits"] = new
-                L["lay"].plan_set(new)
-                for blk in changed:
-                    e, lin = divmod(int(blk), 3)
-                    planes, luts = L["pages"][(e, lin)]
-                    b = int(new[e, lin])
-                    L["lay"].bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
-                L["orc"].set_bits(new)
-        if s not in check_steps:
-            continue
-        epoch = s // cfg.rewrite_every
+            _rewrite_all(cfg, layers, s)
+        # layers (3s .. 3s + 2) mod 24: every layer twice per 16-step plan epoch
+        out_layers = {(per_step * s + i) % n_layers for i in range(per_step)}
         for l, L in enumerate(layers):
             x = synth.tokens(cfg, T, step=s, layer=l)
-            L["lay"].forward(to_dev_f16(x, dev), L["wd"], None, y=y, x_next=x_next, route=route)
+            xd = to_dev_f16(x, dev)
+            L["lay"].forward(xd, L["wd"], None, y=y, x_next=x_next, route=route)
             torch.cuda.synchronize()
-            outputs = s % cfg.rewrite_every == 0 and l % 4 == epoch % 4
+            outputs = l in out_layers
             sub = sample_tokens(T, 1, seed=1000 * s + l) if outputs else np.zeros(0, dtype=np.int32)
             ref = L["orc"].forward(x, L["wr"], None, subset=sub)
             check_routing(route, ref, T, cfg.E, cfg.k)
             if outputs:
-                err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
+                yh = y.cpu().numpy()
+                err = rel_err_per_token(yh[sub], ref["y"][sub])
                 worst = max(worst, float(err.max()))
                 assert err.max() <= REL_TOL, (s, l, err.max())
-        _say(f"stack step {s}: routing exact on all {cfg.layers} layers, worst rel err so far {worst:.3e}")
+                xn_ref = oracle.residual(x, yh)   # O9 on the GPU's own y
+                assert np.array_equal(f16_host(x_next).view(np.uint16), xn_ref.view(np.uint16)), (s, l)
+                seen.add((s // cfg.rewrite_every, l))
+        if s % 4 == 3:
+            _say(f"stack steps 0..{s}: routing exact on all {n_layers} layers, worst rel err {worst:.3e}")
+    n_epochs = (cfg.steps + cfg.rewrite_every - 1) // cfg.rewrite_every
+    assert seen == {(ep, l) for ep in range(n_epochs) for l in range(n_layers)}
     torch.cuda.synchronize()
     for L in layers:
         assert L["lay"].status() == 0
@@ -307,8 +319,7 @@ def test_all_bitwidths_shared_and_ragged(torch_dev):
     and T = 40 > 32 (both kernel variants)."""
     cfg = SMALL
     bits = synth.initial_bits(cfg)
-    for b in range(1, 9):
-        assert (bits == b).any() or True
+    assert sorted(set(int(v) for v in bits.reshape(-1))) == list(range(1, 9)), bits
     blocks = synth.make_layer_blocks(cfg, bits, all_luts=False)
     x, wr, bias = layer_inputs(cfg)
     run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
@@ -387,15 +398,79 @@ def test_plan_rewrite_and_rebind(torch_dev):
 
 
 def test_router_range_flag(torch_dev):
+    """Outside the exact router's range (sum |x w| >= 2^15) or with a non-finite input the device
+    status word raises PW_STATUS_ROUTER_RANGE; reading it clears it."""
     torch, dev = torch_dev
     cfg = synth.CONFIGS["tiny_d256"]
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     lay = gpu_layer(cfg, bits, device_pages(blocks, bits, dev))
     x, wr, _ = layer_inputs(cfg)
+    for bad in ("huge", "inf"):
+        xb = x.copy()
+        if bad == "huge":
+            xb[1, :] = 60000.0     # sum |x w| ~ 60000 * 256 * 0.016 >> 2^15
+        else:
+            xb[2, 7] = np.inf
+        _say(f"router range flag: {bad}")
+        lay.forward(to_dev_f16(xb, dev), to_dev_f16(wr, dev), None)
+        torch.cuda.synchronize()
+        assert lay.status() == 1, bad
+        assert lay.status() == 0       # cleared by the read
+
+
+def test_router_full_fp16_range(torch_dev):
+    """Exact routing for large but in-range inputs. Tokens 0..7 carry 16 columns with |x| in
+    [128, 4096], tokens 8..15 two columns with |x| in [128, 512]; router weights |w| in [128, 512] on
+    4 other columns of every third expert; sum |x w| stays far below 2^15. Routing (ids, weights,
+    counts, offsets, sorted order) must match the oracle's __int128 logits on every token with no
+    range flag. Outputs are compared on tokens 8..15: on tokens 0..7 the SwiGLU output exceeds
+    fp16's range, and the layer rounds it to fp16 as the down projection's MFMA operand."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import route_buffers
+
+    cfg = synth.CONFIGS["tiny_d256"].with_tokens(16)
+    bits = synth.initial_bits(cfg)
+    blocks = _blocks(cfg, bits)
+    x, wr, _ = layer_inputs(cfg)
+    g = np.random.default_rng(77)
     x = x.copy()
-    x[1, 5] = 300.0                # outside the exact-router range
-    lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None)
+    wr = wr.copy()
+    sign = lambda shape: g.choice([-1.0, 1.0], size=shape)
+    x[:8, :16] = (sign((8, 16)) * g.uniform(128, 4096, size=(8, 16))).astype(np.float16)
+    x[8:, 20:22] = (sign((8, 2)) * g.uniform(128, 512, size=(8, 2))).astype(np.float16)
+    wr[::3, 16:20] = (sign(wr[::3, 16:20].shape) * g.uniform(128, 512, size=wr[::3, 16:20].shape)).astype(np.float16)
+    assert float((np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64)).T).max()) < 2 ** 15
+    assert np.abs(x[:8].astype(np.float64)).max() > 2048
+    _say("router full fp16 range")
+    pages = device_pages(blocks, bits, dev)
+    lay = gpu_layer(cfg, bits, pages, max_tokens=16)
+    route = route_buffers(16, cfg.E, cfg.k, dev)
+    y = lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None, route=route)
     torch.cuda.synchronize()
-    assert lay.status() == 1
-    assert lay.status() == 0       # cleared by the read
+    assert lay.status() == 0
+    sub = np.arange(8, 16, dtype=np.int32)
+    ref = oracle.OracleLayer.from_config(cfg, bits, blocks).forward(x, wr, None, subset=sub)
+    assert ref["status"] == 0
+    check_routing(route, ref, 16, cfg.E, cfg.k)
+    err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
+    _say(f"router full fp16 range: routing exact on 16 tokens, max rel err {err.max():.3e} on tokens 8..15")
+    assert err.max() <= REL_TOL
+
+
+LIMITS = synth.MoEConfig("limits", 94, d=8192, E=256, F=128, k=16, T=40, Fs=256,
+                         bits_rule="uniform", bits_values=(3, 4, 5, 6, 8))
+
+
+def test_abi_limits(torch_dev):
+    """The header's limits in one layer: d_model 8192, 256 routed experts, top-16, max_tokens 65536
+    (the workspace at its largest T), plus a shared expert: the router's single-pass offsets scan at
+    E = 256, gate/up items over 8 K-chunks, and the four-tile kernel for the shared expert
+    (T = 40 > 32). All 40 tokens checked."""
+    cfg = LIMITS
+    bits = synth.initial_bits(cfg)
+    _say("ABI limits: generating pages")
+    blocks = _blocks(cfg, bits, workers=16)
+    x, wr, bias = layer_inputs(cfg)
+    _say("ABI limits: d8192 E256 k16 max_tokens 65536")
+    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), max_tokens=65536)
