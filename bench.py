@@ -103,12 +103,12 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
         for (e, lin), blk in blocks.items():
             b = int(bits[e, lin])
             base[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes[:b])).to(dev),
-                              f16(lut_page(blk.luts[b])), b)
+                              f16(lut_page(blk.luts[b]) if args.lut_tiled else blk.luts[b]), b)
         del blocks
         lays = []
         for c in range(M):
             pages = base if c == 0 else {kk: (p.clone(), l.clone(), b) for kk, (p, l, b) in base.items()}
-            lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+            lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T, lut_tiled=args.lut_tiled)
             lay.plan_set(bits)
             for (e, lin), (p, l, b) in pages.items():
                 lay.bind(e, lin, [p[i] for i in range(b)], l, b)
@@ -132,6 +132,7 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
         route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
         lays[0][0].forward(x, wr, bias, y=lays[0][2], route=route, stream=stream)
         torch.cuda.synchronize()
+        check_status([lay for lay, _, _ in lays], label)
         counts = route["expert_count"].cpu().numpy().astype(np.float64)
         flops = 2.0 * 3 * cfg.F * cfg.d * counts.sum() + (2.0 * 3 * cfg.Fs * cfg.d * cfg.T if cfg.Fs else 0.0)
         med = float(np.median(us))
@@ -152,7 +153,7 @@ def sweep(args, torch, synth, PagedMoELayer, lut_page, dev):
               flush=True)
 
 
-def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
+def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev, print_table=True):
     """The whole qwen_stack24_t256 workload: 24 layers, each with its own seeded weights, router and pages, over 64
     decode steps of 256 tokens. Before steps 16, 32 and 48 every layer's plan is rewritten (45 seeded
     blocks lose two bits, not below 3) and the changed blocks are rebound to their lower planes and
@@ -194,9 +195,9 @@ def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
         pages = {}
         for blk in blocks:
             pages[(blk.e, blk.lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes)).to(dev),
-                                       {b: f16(lut_page(v)) for b, v in blk.luts.items()})
+                                       {b: f16(lut_page(v) if args.lut_tiled else v) for b, v in blk.luts.items()})
         del blocks
-        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, T)
+        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, T, lut_tiled=args.lut_tiled)
         lay.plan_set(bits)
         for (e, lin), (p, luts) in pages.items():
             b = int(bits[e, lin])
@@ -239,22 +240,119 @@ def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev):
                                 float(np.mean([Ly["bits"].mean() for Ly in layers]))))
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in evs])
-    print("| plan epoch | steps | mean bits | algorithmic MB per layer | mean step ms | per-layer us | "
-          "GB/s | HBM % | stack tokens/s |")
-    print("|---|---|---|---|---|---|---|---|---|")
+    check_status([Ly["lay"] for Ly in layers], "qwen_stack24_t256")
     n_ep = (cfg.steps + every - 1) // every
+    epochs = []
     for ep in range(n_ep):
         sl = ms[ep * every:(ep + 1) * every]
         mb, bits_mean = epoch_bytes[ep]
-        per_layer_us = sl.mean() * 1e3 / L
-        print(f"| {ep} | {ep * every}..{min(cfg.steps, (ep + 1) * every) - 1} | {bits_mean:.2f} | {mb / 1e6:.1f} | "
-              f"{sl.mean():.2f} | {per_layer_us:.1f} | {mb / (per_layer_us * 1e-6) / 1e9:.0f} | "
-              f"{100 * mb / (per_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.1f} | {T / (sl.mean() * 1e-3):,.0f} |")
-    print(f"| all | 0..{cfg.steps - 1} | | | {ms.mean():.2f} | {ms.mean() * 1e3 / L:.1f} | | | "
-          f"{T * cfg.steps / (ms.sum() * 1e-3):,.0f} |", flush=True)
+        per_layer_us = float(np.median(sl)) * 1e3 / L
+        gbs = mb / (per_layer_us * 1e-6) / 1e9
+        epochs.append({"steps": f"{ep * every}..{min(cfg.steps, (ep + 1) * every) - 1}", "mean_bits": round(bits_mean, 3),
+                       "layer_bytes": mb, "step_ms_median": round(float(np.median(sl)), 4),
+                       "step_ms_p10": round(float(np.percentile(sl, 10)), 4),
+                       "step_ms_p90": round(float(np.percentile(sl, 90)), 4),
+                       "layer_us_median": round(per_layer_us, 2), "layer_GBps": round(gbs, 1),
+                       "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    summary = {"workload": synth.WORKLOAD_TEXT["qwen_stack24_t256"], "tokens_per_step": T, "layers": L,
+               "steps": cfg.steps, "value": round(T * cfg.steps / (ms.sum() * 1e-3), 1), "unit": "tokens/s",
+               "step_ms_median": round(float(np.median(ms)), 4), "step_ms_p10": round(float(np.percentile(ms, 10)), 4),
+               "step_ms_p90": round(float(np.percentile(ms, 90)), 4), "epochs": epochs,
+               "status_checked": True}
+    if print_table:
+        print("| plan epoch | steps | mean bits | algorithmic MB per layer | median step ms | p10 | p90 | per-layer us | "
+              "GB/s | HBM % | stack tokens/s |")
+        print("|---|---|---|---|---|---|---|---|---|---|---|")
+        for ep, e in enumerate(epochs):
+            print(f"| {ep} | {e['steps']} | {e['mean_bits']:.2f} | {e['layer_bytes'] / 1e6:.1f} | {e['step_ms_median']:.2f} | "
+                  f"{e['step_ms_p10']:.2f} | {e['step_ms_p90']:.2f} | {e['layer_us_median']:.1f} | {e['layer_GBps']:.0f} | "
+                  f"{100 * e['layer_hbm_frac']:.1f} | {T / (e['step_ms_median'] * 1e-3):,.0f} |")
+        print(f"| all | 0..{cfg.steps - 1} | | | {summary['step_ms_median']:.2f} | {summary['step_ms_p10']:.2f} | "
+              f"{summary['step_ms_p90']:.2f} | {summary['step_ms_median'] * 1e3 / L:.1f} | | | {summary['value']:,.0f} |",
+              flush=True)
     for Ly in layers:
-        assert Ly["lay"].status() == 0, "layer status flag set"
         Ly["lay"].close()
+    del layers, xs
+    torch.cuda.empty_cache()
+    return summary
+
+
+def check_status(lays, what):
+    """Reads (and clears) the device status word of every layer; a set flag means a forward's output
+    was not valid (router range, or a dependency wait that gave up), so no figure is published."""
+    for lay in lays:
+        flags = lay.status()
+        if flags:
+            log(f"{what}: layer status flags 0x{flags:x} after the timed forwards; no result is reported")
+            sys.exit(3)
+
+
+def make_clones(torch, synth, PagedMoELayer, dev, cfg, n_clones, lut_tiled=False, bits=None, blocks=None):
+    """Pages of one seeded layer, then byte-identical clones at distinct addresses, each bound to its own
+    layer handle. Returns (clones, x_host, wr_host, bias_host, bits, blocks, page_bytes)."""
+    from any_precision_bit_amd.pages import lut_page
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    if bits is None:
+        bits = synth.initial_bits(cfg)
+    if blocks is None:
+        blocks = synth.make_layer_blocks(cfg, bits)
+    x_h = synth.tokens(cfg)
+    wr_h, bias_h = synth.router(cfg)
+    order = lut_page if lut_tiled else np.ascontiguousarray
+    base_pages = {}
+    for (e, lin), blk in blocks.items():
+        b = int(bits[e, lin])
+        base_pages[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes[:b])).to(dev),
+                                f16(order(blk.luts[b])), b)
+    clones = []
+    for c in range(n_clones):
+        pages = base_pages if c == 0 else {key: (p.clone(), l.clone(), b) for key, (p, l, b) in base_pages.items()}
+        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T, lut_tiled=lut_tiled)
+        lay.plan_set(bits)
+        for (e, lin), (p, l, b) in pages.items():
+            lay.bind(e, lin, [p[i] for i in range(b)], l, b)
+        clones.append(dict(lay=lay, pages=pages, x=f16(x_h), wr=f16(wr_h),
+                           bias=None if bias_h is None else f16(bias_h),
+                           y=torch.empty((cfg.T, cfg.d), device=dev)))
+    torch.cuda.synchronize()
+    page_bytes = sum(p.numel() + l.numel() * 2 for (p, l, _) in base_pages.values())
+    return clones, x_h, wr_h, bias_h, bits, blocks, page_bytes
+
+
+def fwd(c, stream):
+    c["lay"].forward(c["x"], c["wr"], c["bias"], y=c["y"], stream=stream)
+
+
+def time_per_call(torch, clones, stream, n, warmup):
+    """Per-call durations (us) of n forwards rotating over the clones, each bracketed by HIP events on
+    the launch stream, after `warmup` untimed forwards."""
+    for i in range(warmup):
+        fwd(clones[i % len(clones)], stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        fwd(clones[i % len(clones)], stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def oracle_rate(oracle, cfg, bits, blocks, x_h, wr_h, bias_h, threads, seconds, subset=None, max_reps=32):
+    """Oracle tokens/s (untuned) over repeated forwards of the batch (or of `subset` of its tokens: the
+    routing of every token plus the expert outputs of those) until `seconds` of oracle time."""
+    lay_o = oracle.OracleLayer.from_config(cfg, bits, blocks)
+    n_tok, t_cpu, reps = 0, 0.0, 0
+    while (t_cpu < seconds or reps == 0) and reps < max_reps:
+        tt = time.perf_counter()
+        lay_o.forward(x_h, wr_h, bias_h, subset=subset, threads=threads)
+        t_cpu += time.perf_counter() - tt
+        n_tok += cfg.T if subset is None else len(subset)
+        reps += 1
+    return n_tok / t_cpu, reps, n_tok, t_cpu
 
 
 def main():
@@ -264,7 +362,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--clones", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-results", action="store_true",
+                    help="headline only: skip the mixtral_d4096 T=1 and qwen_stack24_t256 sub-results")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--lut-tiled", action="store_true", help="LUT pages in the 32-row tiled order")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload shape (per-call median, p10, p90) and print a table")
     ap.add_argument("--only", default="", metavar="LABEL",
@@ -305,40 +406,14 @@ def main():
     cfg = synth.CONFIGS["qwen_d2048_t16"]
     T = cfg.T
     t0 = time.time()
-    bits = synth.initial_bits(cfg)
-    blocks = synth.make_layer_blocks(cfg, bits)
-    x_h = synth.tokens(cfg)
-    wr_h, _ = synth.router(cfg)
-    log(f"generated qwen_d2048_t16 pages in {time.time() - t0:.1f}s")
-
-    def f16(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
-            torch.float16)
-
-    # one set of pages, then byte-identical clones at distinct addresses
-    base_pages = {}
-    for (e, lin), blk in blocks.items():
-        b = int(bits[e, lin])
-        base_pages[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes[:b])).to(dev),
-                                f16(lut_page(blk.luts[b])), b)
-    x = f16(x_h)
-    clones = []
-    for c in range(args.clones):
-        pages = base_pages if c == 0 else {key: (p.clone(), l.clone(), b) for key, (p, l, b) in
-                                           base_pages.items()}
-        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, T)
-        lay.plan_set(bits)
-        for (e, lin), (p, l, b) in pages.items():
-            lay.bind(e, lin, [p[i] for i in range(b)], l, b)
-        clones.append(dict(lay=lay, pages=pages, wr=f16(wr_h), y=torch.empty((T, cfg.d), device=dev)))
-    torch.cuda.synchronize()
-    page_bytes = sum(p.numel() + l.numel() * 2 for (p, l, _) in base_pages.values())
-    log(f"{args.clones} clones x {page_bytes / 1e6:.1f} MB of pages resident")
+    clones, x_h, wr_h, _, bits, blocks, page_bytes = make_clones(torch, synth, PagedMoELayer, dev, cfg,
+                                                                 args.clones, lut_tiled=args.lut_tiled)
+    log(f"qwen_d2048_t16: {args.clones} clones x {page_bytes / 1e6:.1f} MB of pages resident "
+        f"({time.time() - t0:.1f}s)")
 
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
-        c = clones[i % len(clones)]
-        c["lay"].forward(x, c["wr"], None, y=c["y"], stream=stream)
+        fwd(clones[i % len(clones)], stream)
     torch.cuda.synchronize()
 
     # headline: whole forwards back to back, events only around the timed region
@@ -346,8 +421,7 @@ def main():
     wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        c = clones[i % len(clones)]
-        c["lay"].forward(x, c["wr"], None, y=c["y"], stream=stream)
+        fwd(clones[i % len(clones)], stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -367,6 +441,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         avg_ms.append(e0.elapsed_time(e1) / n_rep)
+    check_status([c["lay"] for c in clones], "qwen_d2048_t16")
     nb = clones[0]["lay"].last_bytes(stream)   # route, gate_up, down, residual
     phase_bytes = [nb[0], nb[1] + nb[2]]
     names = ["routing", "experts"]
@@ -385,25 +460,64 @@ def main():
                 "achieved": round(ex_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ex_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": phase_bytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3)}
+    for c in clones:
+        c["lay"].close()
+    del clones
+    torch.cuda.empty_cache()
+
+    # sub-results: the other decode-shaped workloads, same run
+    subs = None
+    if not args.no_sub_results:
+        subs = {}
+        c2 = synth.CONFIGS["mixtral_d4096"].with_tokens(1)
+        t0 = time.time()
+        cl2, *_ = make_clones(torch, synth, PagedMoELayer, dev, c2, args.clones, lut_tiled=args.lut_tiled)
+        log(f"mixtral_d4096 T=1: pages ready ({time.time() - t0:.1f}s)")
+        us = time_per_call(torch, cl2, stream, max(args.steps, 50), args.warmup)
+        check_status([c["lay"] for c in cl2], "mixtral_d4096 T=1")
+        nb2 = cl2[0]["lay"].last_bytes(stream)
+        b2 = nb2[0] + nb2[1] + nb2[2]
+        med = float(np.median(us))
+        subs["mixtral_d4096_t1"] = {
+            "workload": synth.WORKLOAD_TEXT["mixtral_d4096"] + ", T1", "value": round(1 / (med * 1e-6), 1),
+            "unit": "tokens/s", "us_median": round(med, 2), "us_p10": round(float(np.percentile(us, 10)), 2),
+            "us_p90": round(float(np.percentile(us, 90)), 2), "layer_bytes": b2,
+            "layer_GBps": round(b2 / (med * 1e-6) / 1e9, 1), "layer_hbm_frac": round(b2 / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "rotation_clones": args.clones, "calls": int(len(us)), "status_checked": True}
+        for c in cl2:
+            c["lay"].close()
+        del cl2
+        torch.cuda.empty_cache()
+        log(f"mixtral_d4096 T=1: median {med:.1f} us")
+        subs["qwen_stack24_t256"] = layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev, print_table=False)
+        log(f"qwen_stack24_t256: {subs['qwen_stack24_t256']['value']:,.0f} tokens/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
 
-        lay_o = oracle.OracleLayer.from_config(cfg, bits, blocks)
         cores = len(os.sched_getaffinity(0))
         threads = min(cores, 16)
-        n_tok, t_cpu, reps = 0, 0.0, 0
-        while t_cpu < args.cpu_seconds and reps < 32:
-            tt = time.perf_counter()
-            lay_o.forward(x_h, wr_h, None, threads=threads)
-            t_cpu += time.perf_counter() - tt
-            n_tok += T
-            reps += 1
-        cpu = {"value": round(n_tok / t_cpu, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        rate, reps, n_tok, t_cpu = oracle_rate(oracle, cfg, bits, blocks, x_h, wr_h, None, threads, args.cpu_seconds)
+        cpu = {"value": round(rate, 3), "unit": "tokens/s", "cores": cores, "threads": threads, "kind": "oracle",
                "sample": f"{reps} full forward(s) of the same 16-token qwen_d2048_t16 batch ({n_tok} tokens), "
                          f"{t_cpu:.1f}s on {threads} threads"}
-        log(f"oracle: {cpu['value']} tokens/s on {threads} threads")
+        log(f"oracle: {cpu['value']} tokens/s on {threads} threads ({cores} cores in the affinity set)")
+        # one host thread, bounded samples: tiny_d256 (whole batches) and qwen_d2048_t16 (2 of its 16 tokens)
+        one = {}
+        r1, reps1, n1, t1 = oracle_rate(oracle, cfg, bits, blocks, x_h, wr_h, None, 1, 1.0,
+                                        subset=np.array([0, 1], dtype=np.int32), max_reps=1)
+        one["qwen_d2048_t16"] = {"value": round(r1, 3), "unit": "tokens/s",
+                                 "sample": f"routing of all 16 tokens + expert outputs of 2 tokens, {t1:.1f}s"}
+        c0 = synth.CONFIGS["tiny_d256"]
+        bits0 = synth.initial_bits(c0)
+        blocks0 = synth.make_layer_blocks(c0, bits0)
+        wr0, _ = synth.router(c0)
+        r0, reps0, n0, t0c = oracle_rate(oracle, c0, bits0, blocks0, synth.tokens(c0), wr0, None, 1, 1.0)
+        one["tiny_d256"] = {"value": round(r0, 1), "unit": "tokens/s",
+                            "sample": f"{reps0} forward(s) of the 4-token batch, {t0c:.2f}s"}
+        cpu["one_thread"] = one
+        log(f"oracle, one thread: qwen_d2048_t16 {r1:.3f} tokens/s, tiny_d256 {r0:.1f} tokens/s")
 
     out = {
         "metric": "MoE-layer decode tokens/sec on 1 MI355X; achieved HBM GB/s vs peak",
@@ -421,14 +535,14 @@ def main():
         "config": {"workload": "Qwen1.5-MoE-A2.7B-shaped decode layer: d2048, 60 routed experts ffn1408 "
                                "top-4 + shared expert ffn5632, T16, bits U{3,4,5,6,8} per (expert, linear)",
                    "tokens": T, "rotation_clones": args.clones,
+                   "lut_pages": "32-row tiled" if args.lut_tiled else "row-major",
                    "layer_bytes": layer_bytes, "layer_GBps": round(layer_gbs, 1),
-                   "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4)},
+                   "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4), "status_checked": True},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sub_results": subs,
     }
     print(json.dumps(out), flush=True)
-    for c in clones:
-        c["lay"].close()
 
 
 if __name__ == "__main__":
