@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "
                 5: "PW_E_ALIGN", 6: "PW_E_RANGE", 7: "PW_E_STATE", 8: "PW_E_NOMEM", 9: "PW_E_HIP"}
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
             "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
-            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit"]
+            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit",
+            "pw_moe_forward_noalloc"]
 
 
 class PwError(RuntimeError):
@@ -65,6 +66,7 @@ def _load():
         "pw_moe_plan_set": ([P, P, i32], st),
         "pw_page_table_bind": ([P, i32, i32, P, i32, P, i32], st),
         "pw_moe_forward": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
+        "pw_moe_forward_noalloc": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_layer_status": ([P, P, ctypes.POINTER(u32)], st),
         "pw_moe_replay": ([P, i32, P], st),
         "pw_layer_last_bytes": ([P, P, ctypes.POINTER(ctypes.c_double)], st),
@@ -120,6 +122,12 @@ def pw_moe_forward(layer: int, x: int, T: int, router_w: int, router_b, y: int, 
                    route: pw_route_out | None = None, stream: int = 0) -> None:
     _check(lib.pw_moe_forward(layer, x, T, router_w, router_b or None, y, x_next or None,
                               ctypes.byref(route) if route is not None else None, stream or None))
+
+
+def pw_moe_forward_noalloc(layer: int, x: int, T: int, router_w: int, router_b, y: int, x_next=None,
+                           route: pw_route_out | None = None, stream: int = 0) -> None:
+    _check(lib.pw_moe_forward_noalloc(layer, x, T, router_w, router_b or None, y, x_next or None,
+                                      ctypes.byref(route) if route is not None else None, stream or None))
 
 
 def pw_layer_status(layer: int, stream: int = 0) -> int:

@@ -69,6 +69,23 @@ struct DeviceGuard {
     }
 };
 
+// Arguments of every kernel of one forward.
+struct pw_launch {
+    int T = 0;
+    int n_cu = 256;
+    pw::RouteParams rp{};
+    pw::GemmParams gu{}, dn{};
+    const uint16_t* res_x = nullptr;
+    const float* res_y = nullptr;
+    uint16_t* res_out = nullptr;
+};
+
+// Byte offsets of the workspace arrays for forwards of up to T tokens.
+struct WsLayout {
+    size_t o_ids, o_w, o_cnt, o_off, o_srt, o_stk, o_sw, o_pre, o_act, o_st, o_lg, o_dep, total;
+    int T, n_dep, n_counters, dep_stride;
+};
+
 }  // namespace
 
 struct pw_layer_s {
@@ -93,14 +110,12 @@ struct pw_layer_s {
     bool stage_used[kStageSlots] = {};
     int stage_i = 0;
 
-    // launch record of the last forward (for pw_layer_last_bytes and pw_moe_replay)
-    int last_T = 0;
+    // launch record of the last pw_moe_forward (for pw_layer_last_bytes and pw_moe_replay)
+    pw_launch rec{};
     uint32_t wait_limit = 1u << 20;   // polls of a down item's dependency counter
-    pw::RouteParams rp{};
-    pw::GemmParams gp_gu{}, gp_dn{};
-    const uint16_t* res_x = nullptr;
-    const float* res_y = nullptr;
-    uint16_t* res_out = nullptr;
+    // host copy of the page table for pw_moe_forward_noalloc (sized at create)
+    std::vector<DevBlock> shadow;
+    uint32_t* noalloc_status = nullptr;   // status word in the device scratch, once used
 };
 
 namespace {
@@ -148,61 +163,88 @@ void release_device(pw_layer_s* L) {
     L->dev_ready = false;
 }
 
+WsLayout ws_layout(const pw_moe_desc& D, int T) {
+    const int E = D.n_experts, k = D.top_k;
+    const int has_shared = D.d_ffn_shared > 0;
+    const int f_max = std::max(D.d_ffn, D.d_ffn_shared);
+    const size_t act_rows = (size_t)T * k + (size_t)T * has_shared;
+    auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    WsLayout w{};
+    size_t off = 0;
+    w.o_ids = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    w.o_w = off;      off += al(sizeof(float) * (size_t)T * k);
+    w.o_cnt = off;    off += al(sizeof(int32_t) * (size_t)E);
+    w.o_off = off;    off += al(sizeof(int32_t) * ((size_t)E + 1));
+    w.o_srt = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    w.o_stk = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    w.o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
+    w.o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
+    w.o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)f_max);
+    w.o_st = off;     off += al(2 * sizeof(uint32_t));   // status, wait limit
+    w.o_lg = off;     off += al(sizeof(long long) * (size_t)T * E);
+    w.dep_stride = (f_max + pw::kDownPiece - 1) / pw::kDownPiece;
+    w.n_dep = (E + 1) * w.dep_stride + 1;
+    w.n_counters = w.n_dep + T + 1;   // dep, tok_cnt, route_done
+    w.o_dep = off;    off += al(sizeof(uint32_t) * (size_t)w.n_counters);
+    w.total = off;
+    w.T = T;
+    return w;
+}
+
+// The workspace arrays of layout w inside the device buffer at base (256-byte aligned).
+pw::Workspace carve(char* b, const WsLayout& w) {
+    pw::Workspace ws{};
+    ws.ids = (int32_t*)(b + w.o_ids);
+    ws.w = (float*)(b + w.o_w);
+    ws.counts = (int32_t*)(b + w.o_cnt);
+    ws.offsets = (int32_t*)(b + w.o_off);
+    ws.sorted = (int32_t*)(b + w.o_srt);
+    ws.slot_tok = (int32_t*)(b + w.o_stk);
+    ws.slot_w = (float*)(b + w.o_sw);
+    ws.prefix = (int32_t*)(b + w.o_pre);
+    ws.act = (uint16_t*)(b + w.o_act);
+    ws.status = (uint32_t*)(b + w.o_st);
+    ws.wait_limit = ws.status + 1;
+    ws.lg = (long long*)(b + w.o_lg);
+    ws.dep = (uint32_t*)(b + w.o_dep);
+    ws.tok_cnt = ws.dep + w.n_dep;
+    ws.route_done = ws.tok_cnt + w.T;
+    ws.dep_stride = w.dep_stride;
+    return ws;
+}
+
+// Compute units of a device, read once per device.
+pw_status device_cus(int dev, int* n_cu) {
+    static int cached[64] = {};
+    if (dev < 0 || dev >= 64) return fail(PW_E_ARG, "device %d", dev);
+    if (cached[dev] <= 0) {
+        int cus = 0;
+        const hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "device attribute");
+        cached[dev] = cus > 0 ? cus : 256;
+    }
+    *n_cu = cached[dev];
+    return PW_OK;
+}
+
 pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
     if (L->dev_ready) return PW_OK;
     const pw_moe_desc& D = L->desc;
-    const int T = D.max_tokens, E = D.n_experts, k = D.top_k, d = D.d_model;
-    const int has_shared = D.d_ffn_shared > 0;
     L->f_max = std::max(D.d_ffn, D.d_ffn_shared);
-    const size_t act_rows = (size_t)T * k + (size_t)T * has_shared;
-    auto al = [](size_t n) { return (n + 255) & ~(size_t)255; };
-    size_t off = 0;
-    const size_t o_ids = off;    off += al(sizeof(int32_t) * (size_t)T * k);
-    const size_t o_w = off;      off += al(sizeof(float) * (size_t)T * k);
-    const size_t o_cnt = off;    off += al(sizeof(int32_t) * (size_t)E);
-    const size_t o_off = off;    off += al(sizeof(int32_t) * ((size_t)E + 1));
-    const size_t o_srt = off;    off += al(sizeof(int32_t) * (size_t)T * k);
-    const size_t o_stk = off;    off += al(sizeof(int32_t) * (size_t)T * k);
-    const size_t o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
-    const size_t o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
-    const size_t o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)L->f_max);
-    const size_t o_st = off;     off += al(2 * sizeof(uint32_t));   // status, wait limit
-    const size_t o_lg = off;     off += al(sizeof(long long) * (size_t)T * E);
-    const int dep_stride = (L->f_max + pw::kDownPiece - 1) / pw::kDownPiece;
-    const int n_dep = (E + 1) * dep_stride + 1;
-    const int n_counters = n_dep + T + 1;   // dep, tok_cnt, route_done
-    const size_t o_dep = off;    off += al(sizeof(uint32_t) * (size_t)n_counters);
+    const WsLayout lay = ws_layout(D, D.max_tokens);
     hipError_t e;
-    int cus = 0;
-    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device)) != hipSuccess)
-        return hip_fail(e, "device attribute");
-    L->n_cu = cus > 0 ? cus : 256;
-    if ((e = hipMalloc((void**)&L->d_ws, off)) != hipSuccess) {
+    pw_status st = device_cus(L->device, &L->n_cu);
+    if (st != PW_OK) return st;
+    if ((e = hipMalloc((void**)&L->d_ws, lay.total)) != hipSuccess) {
         L->d_ws = nullptr;
-        return fail(PW_E_NOMEM, "workspace (%zu bytes): %s", off, hipGetErrorString(e));
+        return fail(PW_E_NOMEM, "workspace (%zu bytes): %s", lay.total, hipGetErrorString(e));
     }
     if ((e = hipMalloc((void**)&L->d_blocks, sizeof(DevBlock) * n_blocks(L))) != hipSuccess) {
         L->d_blocks = nullptr;
         release_device(L);
         return fail(PW_E_NOMEM, "page table: %s", hipGetErrorString(e));
     }
-    char* b = L->d_ws;
-    L->ws.ids = (int32_t*)(b + o_ids);
-    L->ws.w = (float*)(b + o_w);
-    L->ws.counts = (int32_t*)(b + o_cnt);
-    L->ws.offsets = (int32_t*)(b + o_off);
-    L->ws.sorted = (int32_t*)(b + o_srt);
-    L->ws.slot_tok = (int32_t*)(b + o_stk);
-    L->ws.slot_w = (float*)(b + o_sw);
-    L->ws.prefix = (int32_t*)(b + o_pre);
-    L->ws.act = (uint16_t*)(b + o_act);
-    L->ws.status = (uint32_t*)(b + o_st);
-    L->ws.wait_limit = L->ws.status + 1;
-    L->ws.lg = (long long*)(b + o_lg);
-    L->ws.dep = (uint32_t*)(b + o_dep);
-    L->ws.tok_cnt = L->ws.dep + n_dep;
-    L->ws.route_done = L->ws.tok_cnt + T;
-    L->ws.dep_stride = dep_stride;
+    L->ws = carve(L->d_ws, lay);
     for (int i = 0; i < kStageSlots; ++i) {
         if ((e = hipHostMalloc((void**)&L->h_stage[i], sizeof(DevBlock) * n_blocks(L), hipHostMallocDefault)) !=
             hipSuccess) {
@@ -216,12 +258,25 @@ pw_status ensure_device(pw_layer_s* L, hipStream_t s) {
             return hip_fail(e, "hipEventCreate");
         }
     }
-    if ((e = pw::launch_init_ws(L->ws, n_counters, L->wait_limit, s)) != hipSuccess) {
+    if ((e = pw::launch_init_ws(L->ws, lay.n_counters, L->wait_limit, s)) != hipSuccess) {
         release_device(L);
         return hip_fail(e, "init workspace");
     }
     L->dev_ready = true;
     return PW_OK;
+}
+
+// The device page table entries of every block: plane p goes to slot p + 8 - b,
+// so slot s always carries bit 7 - s of the index.
+void fill_tables(const pw_layer_s* L, DevBlock* h) {
+    for (int i = 0; i < n_blocks(L); ++i) {
+        const Page& pg = L->pages[i];
+        DevBlock& db = h[i];
+        std::memset(&db, 0, sizeof db);
+        db.bits = L->bits[i];
+        for (int p = 0; p < db.bits; ++p) db.planes[p + 8 - db.bits] = (uint64_t)(uintptr_t)pg.planes[p];
+        db.lut = (uint64_t)(uintptr_t)pg.lut;
+    }
 }
 
 pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
@@ -231,15 +286,7 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
     if (L->stage_used[slot] && (e = hipEventSynchronize(L->stage_ev[slot])) != hipSuccess)
         return hip_fail(e, "staging event");
     DevBlock* h = L->h_stage[slot];
-    for (int i = 0; i < n_blocks(L); ++i) {
-        const Page& pg = L->pages[i];
-        DevBlock& db = h[i];
-        std::memset(&db, 0, sizeof db);
-        db.bits = L->bits[i];
-        // plane p goes to slot p + 8 - b, so slot s always carries bit 7 - s of the index
-        for (int p = 0; p < db.bits; ++p) db.planes[p + 8 - db.bits] = (uint64_t)(uintptr_t)pg.planes[p];
-        db.lut = (uint64_t)(uintptr_t)pg.lut;
-    }
+    fill_tables(L, h);
     if ((e = hipMemcpyAsync(L->d_blocks, h, sizeof(DevBlock) * n_blocks(L), hipMemcpyHostToDevice, s)) !=
         hipSuccess)
         return hip_fail(e, "table upload");
@@ -251,38 +298,139 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
 }
 
 
-// Enqueues the kernels of one phase of the forward recorded in L:
-// 0 routing (router + bucket sort), 1 experts (gate_up + SwiGLU + down +
-// accumulation), 2 residual hand-off.
-pw_status launch_phase(pw_layer_s* L, int phase, hipStream_t s) {
-    const int T = L->last_T;
+// Kernel arguments of one forward on T tokens with workspace ws, device page
+// table blocks and the shared expert's act rows from shared_base on.
+pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* router_w, const void* router_b,
+                      float* y, void* x_next, const pw_route_out* route, const pw::Workspace& ws,
+                      const DevBlock* blocks, int shared_base, int n_cu) {
+    const pw_moe_desc& D = L->desc;
+    const int E = D.n_experts, k = D.top_k, d = D.d_model;
+    const int has_shared = D.d_ffn_shared > 0;
+    const int f_max = std::max(D.d_ffn, D.d_ffn_shared);
+    pw_launch r{};
+    r.T = T;
+    r.n_cu = n_cu;
+    pw::RouteParams& rp = r.rp;
+    rp.x = (const uint16_t*)x;
+    rp.wr = (const uint16_t*)router_w;
+    rp.bias = (const uint16_t*)router_b;
+    rp.T = T;
+    rp.d = d;
+    rp.E = E;
+    rp.k = k;
+    rp.ws = ws;
+    rp.y = y;
+    rp.has_shared = has_shared;
+    rp.tiles_gu_r = D.d_ffn / 32;
+    rp.tiles_gu_s = D.d_ffn_shared / 32;
+    rp.tiles_dn = d / 64;
+    rp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
+    rp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
+    if (route) {
+        rp.o_ids = route->topk_ids;
+        rp.o_w = route->topk_w;
+        rp.o_counts = route->expert_count;
+        rp.o_offsets = route->expert_offset;
+        rp.o_sorted = route->sorted_assign;
+    }
+    pw::GemmParams gp{};
+    gp.blocks = blocks;
+    gp.E = E;
+    gp.k = k;
+    gp.T = T;
+    gp.d = d;
+    gp.F = D.d_ffn;
+    gp.Fs = D.d_ffn_shared;
+    gp.has_shared = has_shared;
+    gp.ws = ws;
+    gp.ld_act = f_max;
+    gp.shared_base = shared_base;
+    gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
+    gp.y = y;
+    // gate_up + SwiGLU: items of 32 rows of F (gate and up)
+    r.gu = gp;
+    r.gu.tiles_r = D.d_ffn / 32;
+    r.gu.tiles_s = D.d_ffn_shared / 32;
+    r.gu.pieces_r = r.gu.pieces_s = 1;
+    r.gu.x = (const uint16_t*)x;
+    r.gu.b_bytes = (uint32_t)((size_t)T * d * 2);
+    // down + weighted scatter-accumulate: items of 64 rows of d
+    r.dn = gp;
+    r.dn.tiles_r = d / 64;
+    r.dn.tiles_s = has_shared ? d / 64 : 0;
+    r.dn.pieces_r = rp.pieces_dn_r;
+    r.dn.pieces_s = has_shared ? rp.pieces_dn_s : 1;
+    r.dn.b_bytes = (uint32_t)(((size_t)shared_base + (size_t)T * has_shared) * f_max * 2);
+    r.res_x = (const uint16_t*)x;
+    r.res_y = y;
+    r.res_out = (uint16_t*)x_next;
+    return r;
+}
+
+// Enqueues the kernels of one phase of a forward: 0 routing (router + bucket
+// sort), 1 experts (gate_up + SwiGLU + down + accumulation), 2 residual hand-off.
+pw_status launch_phase(const pw_launch& r, int d_model, int phase, hipStream_t s) {
+    const int T = r.T;
     hipError_t e = hipSuccess;
     switch (phase) {
         case 0:
-            if ((e = pw::launch_route(L->rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
+            if ((e = pw::launch_route(r.rp, s)) != hipSuccess) return hip_fail(e, "route kernel");
             break;
         case 1: {
-            pw::ExpertParams ep{L->gp_gu, L->gp_dn};
+            pw::ExpertParams ep{r.gu, r.dn};
             ep.gu.list = pw::LIST_GU_SMALL;
             ep.dn.list = pw::LIST_DN_SMALL;
-            if ((e = pw::launch_experts(pw::kSmallTokens, ep, L->n_cu, s)) != hipSuccess)
+            if ((e = pw::launch_experts(pw::kSmallTokens, ep, r.n_cu, s)) != hipSuccess)
                 return hip_fail(e, "expert kernel");
             if (T > pw::kSmallMax) {
                 ep.gu.list = pw::LIST_GU_LARGE;
                 ep.dn.list = pw::LIST_DN_LARGE;
-                if ((e = pw::launch_experts(pw::kLargeTokens, ep, L->n_cu, s)) != hipSuccess)
+                if ((e = pw::launch_experts(pw::kLargeTokens, ep, r.n_cu, s)) != hipSuccess)
                     return hip_fail(e, "expert kernel (large)");
             }
             break;
         }
         case 2:
-            if (L->res_out &&
-                (e = pw::launch_residual(L->res_x, L->res_y, L->res_out, (long)T * L->desc.d_model, s)) !=
-                    hipSuccess)
+            if (r.res_out && (e = pw::launch_residual(r.res_x, r.res_y, r.res_out, (long)T * d_model, s)) != hipSuccess)
                 return hip_fail(e, "residual kernel");
             break;
         default:
             return fail(PW_E_ARG, "phase %d not in 0..2", phase);
+    }
+    return PW_OK;
+}
+
+// Argument checks shared by both forward entry points (no HIP call).
+pw_status check_forward(const pw_layer_s* L, const void* x, int32_t T, const void* router_w, const void* router_b,
+                        const float* y, const void* x_next, const pw_route_out* route) {
+    const pw_moe_desc& D = L->desc;
+    if (T < 0 || T > D.max_tokens) return fail(PW_E_RANGE, "T=%d not in 0..max_tokens=%d", T, D.max_tokens);
+    pw_status st = validate_tables(L);
+    if (st != PW_OK) return st;
+    if (T == 0) return PW_OK;
+    if (!x || !router_w || !y) return fail(PW_E_ARG, "pw_moe_forward: null x, router_w or y");
+    if (!aligned16(x) || !aligned16(router_w) || !aligned16(y) || (x_next && !aligned16(x_next)))
+        return fail(PW_E_ALIGN, "x, router_w, y and x_next must be 16-byte aligned");
+    if (router_b && (reinterpret_cast<uintptr_t>(router_b) & 1u))
+        return fail(PW_E_ALIGN, "router_b must be 2-byte aligned");
+    if (route) {
+        const void* rp[5] = {route->topk_ids, route->topk_w, route->expert_count, route->expert_offset,
+                             route->sorted_assign};
+        for (const void* q : rp)
+            if (q && (reinterpret_cast<uintptr_t>(q) & 3u))
+                return fail(PW_E_ALIGN, "route outputs must be 4-byte aligned");
+    }
+    return PW_OK;
+}
+
+pw_status enqueue_all(const pw_launch& r, int d_model, hipStream_t s) {
+    pw_status st;
+    for (int phase = 0; phase < 3; ++phase)
+        if ((st = launch_phase(r, d_model, phase, s)) != PW_OK) return st;
+    static const bool debug_sync = getenv("PW_DEBUG_SYNC") != nullptr;   // read once per process
+    if (debug_sync) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "pw_moe_forward (debug sync)");
     }
     return PW_OK;
 }
@@ -324,6 +472,7 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     L->desc = D;
     L->n_total = D.n_experts + (D.d_ffn_shared > 0 ? 1 : 0);
     L->pages.resize((size_t)n_blocks(L));
+    L->shadow.resize((size_t)n_blocks(L));
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     L->device = dev;
@@ -384,23 +533,8 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
                          float* y, void* x_next, const pw_route_out* route, void* stream) {
     g_err.clear();
     if (!L) return fail(PW_E_ARG, "pw_moe_forward: null layer");
-    const pw_moe_desc& D = L->desc;
-    if (T < 0 || T > D.max_tokens) return fail(PW_E_RANGE, "T=%d not in 0..max_tokens=%d", T, D.max_tokens);
-    pw_status st = validate_tables(L);
-    if (st != PW_OK) return st;
-    if (T == 0) return PW_OK;
-    if (!x || !router_w || !y) return fail(PW_E_ARG, "pw_moe_forward: null x, router_w or y");
-    if (!aligned16(x) || !aligned16(router_w) || !aligned16(y) || (x_next && !aligned16(x_next)))
-        return fail(PW_E_ALIGN, "x, router_w, y and x_next must be 16-byte aligned");
-    if (router_b && (reinterpret_cast<uintptr_t>(router_b) & 1u))
-        return fail(PW_E_ALIGN, "router_b must be 2-byte aligned");
-    if (route) {
-        const void* rp[5] = {route->topk_ids, route->topk_w, route->expert_count, route->expert_offset,
-                             route->sorted_assign};
-        for (const void* q : rp)
-            if (q && (reinterpret_cast<uintptr_t>(q) & 3u))
-                return fail(PW_E_ALIGN, "route outputs must be 4-byte aligned");
-    }
+    pw_status st = check_forward(L, x, T, router_w, router_b, y, x_next, route);
+    if (st != PW_OK || T == 0) return st;
     DeviceGuard guard(L->device);
     if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
     hipStream_t s = (hipStream_t)stream;
@@ -411,107 +545,87 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     }
     if ((st = ensure_device(L, s)) != PW_OK) return st;
     if ((st = upload_tables(L, s)) != PW_OK) return st;
-
-    const int E = D.n_experts, k = D.top_k, d = D.d_model;
-    const int has_shared = D.d_ffn_shared > 0;
-    L->last_T = T;
-
-    pw::RouteParams& rp = L->rp;
-    rp = pw::RouteParams{};
-    rp.x = (const uint16_t*)x;
-    rp.wr = (const uint16_t*)router_w;
-    rp.bias = (const uint16_t*)router_b;
-    rp.T = T;
-    rp.d = d;
-    rp.E = E;
-    rp.k = k;
-    rp.ws = L->ws;
-    rp.y = y;
-    rp.has_shared = has_shared;
-    rp.tiles_gu_r = D.d_ffn / 32;
-    rp.tiles_gu_s = D.d_ffn_shared / 32;
-    rp.tiles_dn = d / 64;
-    rp.pieces_dn_r = (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece;
-    rp.pieces_dn_s = (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece;
-    if (route) {
-        rp.o_ids = route->topk_ids;
-        rp.o_w = route->topk_w;
-        rp.o_counts = route->expert_count;
-        rp.o_offsets = route->expert_offset;
-        rp.o_sorted = route->sorted_assign;
-    }
-    pw::GemmParams gp{};
-    gp.blocks = L->d_blocks;
-    gp.E = E;
-    gp.k = k;
-    gp.T = T;
-    gp.d = d;
-    gp.F = D.d_ffn;
-    gp.Fs = D.d_ffn_shared;
-    gp.has_shared = has_shared;
-    gp.ws = L->ws;
-    gp.ld_act = L->f_max;
-    gp.shared_base = D.max_tokens * k;
-    gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
-    gp.y = y;
-    // gate_up + SwiGLU: items of 32 rows of F (gate and up)
-    L->gp_gu = gp;
-    L->gp_gu.tiles_r = D.d_ffn / 32;
-    L->gp_gu.tiles_s = D.d_ffn_shared / 32;
-    L->gp_gu.pieces_r = L->gp_gu.pieces_s = 1;
-    L->gp_gu.x = (const uint16_t*)x;
-    L->gp_gu.b_bytes = (uint32_t)((size_t)T * d * 2);
-    // down + weighted scatter-accumulate: items of 64 rows of d
-    L->gp_dn = gp;
-    L->gp_dn.tiles_r = d / 64;
-    L->gp_dn.tiles_s = has_shared ? d / 64 : 0;
-    L->gp_dn.pieces_r = rp.pieces_dn_r;
-    L->gp_dn.pieces_s = has_shared ? rp.pieces_dn_s : 1;
-    L->gp_dn.b_bytes = (uint32_t)(((size_t)D.max_tokens * k + (size_t)D.max_tokens * has_shared) * L->f_max * 2);
-    L->res_x = (const uint16_t*)x;
-    L->res_y = y;
-    L->res_out = (uint16_t*)x_next;
-
-    for (int phase = 0; phase < 3; ++phase) {
-        if ((st = launch_phase(L, phase, s)) != PW_OK) {
-            L->dirty = true;   // the runtime refused a launch: upload the tables again next time
-            return st;
-        }
-    }
-    static const bool debug_sync = getenv("PW_DEBUG_SYNC") != nullptr;   // read once per process
-    if (debug_sync) {
-        hipError_t e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return hip_fail(e, "pw_moe_forward (debug sync)");
+    L->rec = make_launch(L, x, T, router_w, router_b, y, x_next, route, L->ws, L->d_blocks,
+                         L->desc.max_tokens * L->desc.top_k, L->n_cu);
+    if ((st = enqueue_all(L->rec, L->desc.d_model, s)) != PW_OK) {
+        L->dirty = true;   // the runtime refused a launch: upload the tables again next time
+        return st;
     }
     return PW_OK;
+}
+
+pw_status pw_moe_forward_noalloc(pw_layer L, const void* x, int32_t T, const void* router_w,
+                                 const void* router_b, float* y, void* x_next, const pw_route_out* route,
+                                 void* stream) {
+    g_err.clear();
+    if (!L) return fail(PW_E_ARG, "pw_moe_forward_noalloc: null layer");
+    pw_status st = check_forward(L, x, T, router_w, router_b, y, x_next, route);
+    if (st != PW_OK || T == 0) return st;
+    // scratch = [page table][workspace for T tokens]
+    const size_t table_bytes = (sizeof(DevBlock) * (size_t)n_blocks(L) + 255) & ~(size_t)255;
+    const WsLayout lay = ws_layout(L->desc, T);
+    if (table_bytes + lay.total > pw::kScratchBytes)
+        return fail(PW_E_RANGE, "pw_moe_forward_noalloc: T=%d needs %zu bytes of device scratch, the static scratch "
+                    "holds %zu", T, table_bytes + lay.total, (size_t)pw::kScratchBytes);
+    DeviceGuard guard(L->device);
+    if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
+    hipStream_t s = (hipStream_t)stream;
+    char* scratch = nullptr;
+    size_t cap = 0;
+    hipError_t e = pw::scratch_memory(L->device, (void**)&scratch, &cap);
+    if (e != hipSuccess) return hip_fail(e, "device scratch address");
+    if ((e = pw::prepare_experts()) != hipSuccess) return hip_fail(e, "expert kernel set-up");
+    int n_cu = 0;
+    if ((st = device_cus(L->device, &n_cu)) != PW_OK) return st;
+    DevBlock* d_blocks = (DevBlock*)scratch;
+    const pw::Workspace ws = carve(scratch + table_bytes, lay);
+    // the page table from the layer's host copy (pageable: consumed before the copy call returns)
+    fill_tables(L, L->shadow.data());
+    if ((e = hipMemcpyAsync(d_blocks, L->shadow.data(), sizeof(DevBlock) * (size_t)n_blocks(L),
+                            hipMemcpyHostToDevice, s)) != hipSuccess)
+        return hip_fail(e, "table upload");
+    // the scratch keeps the last call's contents: counters and status start from zero
+    if ((e = pw::launch_init_ws(ws, lay.n_counters, L->wait_limit, s)) != hipSuccess)
+        return hip_fail(e, "scratch init");
+    L->noalloc_status = ws.status;
+    const pw_launch r = make_launch(L, x, T, router_w, router_b, y, x_next, route, ws, d_blocks, T * L->desc.top_k,
+                                    n_cu);
+    return enqueue_all(r, L->desc.d_model, s);
 }
 
 pw_status pw_moe_replay(pw_layer L, int32_t phase, void* stream) {
     g_err.clear();
     if (!L) return fail(PW_E_ARG, "pw_moe_replay: null layer");
-    if (!L->dev_ready || L->last_T == 0) return fail(PW_E_STATE, "pw_moe_replay: no forward has run");
+    if (!L->dev_ready || L->rec.T == 0) return fail(PW_E_STATE, "pw_moe_replay: no forward has run");
     if (phase < 0 || phase > 2) return fail(PW_E_ARG, "phase %d not in 0..2", phase);
     DeviceGuard guard(L->device);
     if (!guard.ok) return fail(PW_E_HIP, "cannot select device %d", L->device);
-    return launch_phase(L, phase, (hipStream_t)stream);
+    return launch_phase(L->rec, L->desc.d_model, phase, (hipStream_t)stream);
 }
 
 pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
     g_err.clear();
     if (!L || !flags) return fail(PW_E_ARG, "pw_layer_status: null argument");
     *flags = 0;
-    if (!L->dev_ready) return PW_OK;
+    if (!L->dev_ready && !L->noalloc_status) return PW_OK;
     DeviceGuard guard(L->device);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // the layer's own workspace, and the device scratch if it ran no-alloc forwards
+    uint32_t* words[2] = {L->dev_ready ? L->ws.status : nullptr, L->noalloc_status};
     uint32_t v = 0;
-    if ((e = hipMemcpyAsync(&v, L->ws.status, sizeof v, hipMemcpyDeviceToHost, s)) != hipSuccess)
-        return hip_fail(e, "status read");
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "status sync");
-    if (v) {
-        const uint32_t zero = 0;
-        if ((e = hipMemcpy(L->ws.status, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess)
-            return hip_fail(e, "status clear");
+    for (uint32_t* w : words) {
+        if (!w) continue;
+        uint32_t u = 0;
+        if ((e = hipMemcpyAsync(&u, w, sizeof u, hipMemcpyDeviceToHost, s)) != hipSuccess)
+            return hip_fail(e, "status read");
+        if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "status sync");
+        if (u) {
+            const uint32_t zero = 0;
+            if ((e = hipMemcpy(w, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess)
+                return hip_fail(e, "status clear");
+        }
+        v |= u;
     }
     *flags = v;
     if (v)
@@ -524,10 +638,10 @@ pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
 pw_status pw_layer_last_bytes(pw_layer L, void* stream, double* bytes) {
     g_err.clear();
     if (!L || !bytes) return fail(PW_E_ARG, "pw_layer_last_bytes: null argument");
-    if (!L->dev_ready || L->last_T == 0) return fail(PW_E_STATE, "no forward has run");
+    if (!L->dev_ready || L->rec.T == 0) return fail(PW_E_STATE, "no forward has run");
     DeviceGuard guard(L->device);
     const pw_moe_desc& D = L->desc;
-    const int E = D.n_experts, T = L->last_T, d = D.d_model;
+    const int E = D.n_experts, T = L->rec.T, d = D.d_model;
     std::vector<int32_t> cnt((size_t)E);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

@@ -111,6 +111,11 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, 
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int lut_tiled, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
+// Device scratch of the no-allocation forward: the device address of the
+// static array on device dev (which must be current) and its size.
+constexpr size_t kScratchBytes = 32u << 20;
+hipError_t scratch_memory(int dev, void** ptr, size_t* bytes);
+
 // LDS bytes of the expert kernel for items of tile_tokens tokens.
 int expert_lds_bytes(int tile_tokens);
 

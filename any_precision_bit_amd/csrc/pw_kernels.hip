@@ -36,6 +36,7 @@
 
 #include <climits>
 #include <cstdlib>
+#include <mutex>
 
 #include "pw.h"
 #include "pw_internal.h"
@@ -1171,6 +1172,32 @@ __global__ __launch_bounds__(64) void debug_kernel(DebugParams p) {
             }
         }
     }
+}
+
+// ============================================================================ static scratch
+
+// Device scratch of pw_moe_forward_noalloc: the page table and the workspace of
+// one forward live here instead of in memory the library allocates. Each GPU
+// holds its own copy from module load until the process ends; every no-alloc
+// call on that GPU shares it.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on device dev (the host-side name is only a
+// stand-in), looked up once per device with that device current.
+hipError_t scratch_memory(int dev, void** ptr, size_t* bytes) {
+    static void* addr[64] = {};
+    static std::mutex mu;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kScratchBytes;
+    return hipSuccess;
 }
 
 // ============================================================================ launchers

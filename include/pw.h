@@ -168,6 +168,31 @@ pw_status pw_moe_forward(pw_layer layer, const void* x, int32_t T, const void* r
                          const void* router_b, float* y, void* x_next,
                          const pw_route_out* route, void* stream);
 
+/* For callers that cannot allocate memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. The same forward as
+ * pw_moe_forward (same arguments, kernels and results), but it calls no
+ * hipMalloc, hipFree, hipHostMalloc or other allocating routine: the device
+ * page table and the forward's workspace live in a static device array of
+ * 32 MiB (per GPU, held from library load until the process ends) instead of
+ * the layer's own device memory, which is neither allocated nor used.
+ *   - T is limited by that array: the page table plus a workspace for T tokens
+ *     must fit (about (T*top_k + T*has_shared) * max(d_ffn, d_ffn_shared) * 2
+ *     bytes plus T * n_experts * 8); PW_E_RANGE otherwise, with the sizes in
+ *     pw_last_error(). The 24-layer qwen shape (T = 256, top-4, ffn 5632)
+ *     needs 15 MB.
+ *   - Every call on one GPU shares the array, which keeps the last call's
+ *     contents; each call zeroes the counters and the status word it uses
+ *     before its kernels. Calls that overlap in time on one GPU (on different
+ *     streams, or from different threads) race and give undefined results.
+ *   - The page table is copied from host memory the layer owns (pageable),
+ *     which the copy call consumes before it returns.
+ *   - pw_layer_status reports the status word of the last no-alloc call on the
+ *     layer's GPU as well as the layer's own; pw_moe_replay and
+ *     pw_layer_last_bytes refer to the last pw_moe_forward only. */
+pw_status pw_moe_forward_noalloc(pw_layer layer, const void* x, int32_t T, const void* router_w,
+                                 const void* router_b, float* y, void* x_next,
+                                 const pw_route_out* route, void* stream);
+
 /* Synchronises `stream`, then reads and clears the device status word into
  * *flags (PW_STATUS_* bits). Returns PW_E_STATE if any flag was set. */
 pw_status pw_layer_status(pw_layer layer, void* stream, uint32_t* flags);

@@ -171,3 +171,33 @@ def test_wait_limit_hook(B):
     finally:
         B.pw_layer_destroy(h)
 
+
+
+def test_noalloc_validation(B):
+    """pw_moe_forward_noalloc checks its arguments and the static scratch size before any HIP call."""
+    with pytest.raises(B.PwError) as ei:
+        B.pw_moe_forward_noalloc(0, 4096, 1, 4096, 0, 4096)
+    assert ei.value.status == 1
+    # the 24-layer qwen shape at T = 1024 needs ~58 MB of workspace: beyond the 32 MiB scratch
+    h = B.pw_layer_create(2048, 60, 1408, 4, 5632, 1024)
+    try:
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_forward_noalloc(h, 4096, 1, 4096, 0, 4096)
+        assert ei.value.status == 7                     # no plan yet
+        B.pw_moe_plan_set(h, [3] * (3 * 61))
+        base = 1 << 40
+        for e in range(61):
+            for lin in range(3):
+                B.pw_page_table_bind(h, e, lin, [base + 4096 * p for p in range(3)], base + (1 << 20), 3)
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_forward_noalloc(h, 4096, 1025, 4096, 0, 4096)
+        assert ei.value.status == 6                     # T above max_tokens
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_forward_noalloc(h, 4097, 16, 4096, 0, 4096)
+        assert ei.value.status == 5                     # misaligned x
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_forward_noalloc(h, 4096, 1024, 4096, 0, 4096)
+        assert ei.value.status == 6 and "scratch" in str(ei.value)
+        B.pw_moe_forward_noalloc(h, 4096, 0, 4096, 0, 4096)   # T = 0: a no-op
+    finally:
+        B.pw_layer_destroy(h)
