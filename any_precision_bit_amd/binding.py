@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
             "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
             "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit",
-            "pw_moe_forward_noalloc"]
+            "pw_moe_forward_noalloc", "pw_plan_greedy"]
 
 
 class PwError(RuntimeError):
@@ -68,6 +68,7 @@ def _load():
         "pw_moe_forward": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_moe_forward_noalloc": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_layer_status": ([P, P, ctypes.POINTER(u32)], st),
+        "pw_plan_greedy": ([P, P, P, P, i32, P, P, ctypes.c_double, P, P], st),
         "pw_moe_replay": ([P, i32, P], st),
         "pw_layer_last_bytes": ([P, P, ctypes.POINTER(ctypes.c_double)], st),
         "pw_debug_unpack": ([P, i32, i32, i32, P, P], st),
@@ -128,6 +129,24 @@ def pw_moe_forward_noalloc(layer: int, x: int, T: int, router_w: int, router_b, 
                            route: pw_route_out | None = None, stream: int = 0) -> None:
     _check(lib.pw_moe_forward_noalloc(layer, x, T, router_w, router_b or None, y, x_next or None,
                                       ctypes.byref(route) if route is not None else None, stream or None))
+
+
+def pw_plan_greedy(layer: int, sensitivity, expert_count, n_tokens: int, bytes_to_free: float,
+                   residual=None, min_bits=None, max_bits=None):
+    """Host arrays in, (new bits u8 [n_blocks], bytes moved, damage, actions) out."""
+    import numpy as np
+
+    sens = np.ascontiguousarray(sensitivity, dtype=np.float32).reshape(-1)
+    cnt = np.ascontiguousarray(expert_count, dtype=np.int32).reshape(-1)
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32).reshape(-1)
+    lo = None if min_bits is None else np.ascontiguousarray(min_bits, dtype=np.uint8).reshape(-1)
+    hi = None if max_bits is None else np.ascontiguousarray(max_bits, dtype=np.uint8).reshape(-1)
+    out = np.zeros(sens.shape[0], dtype=np.uint8)
+    r = (ctypes.c_double * 3)()
+    p = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib.pw_plan_greedy(layer, p(sens), p(res), p(cnt), n_tokens, p(lo), p(hi), float(bytes_to_free),
+                              p(out), r))
+    return out, r[0], r[1], int(r[2])
 
 
 def pw_layer_status(layer: int, stream: int = 0) -> int:

@@ -4,7 +4,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "pw_api.cpp"), os.path.join(HERE, "csrc", "pw_kernels.hip")]
+SRCS = [os.path.join(HERE, "csrc", "pw_api.cpp"), os.path.join(HERE, "csrc", "pw_plan.cpp"),
+        os.path.join(HERE, "csrc", "pw_kernels.hip")]
 LIB = os.path.join(HERE, "libpw.so")
 
 HIPCC_FLAGS = [

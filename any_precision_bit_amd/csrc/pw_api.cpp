@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <array>
 #include <cstdarg>
 #include <cstdio>
@@ -632,6 +633,46 @@ pw_status pw_layer_status(pw_layer L, void* stream, uint32_t* flags) {
         return fail(PW_E_STATE, "device status flags 0x%x (%s%s)", v,
                     (v & PW_STATUS_ROUTER_RANGE) ? "router range " : "",
                     (v & PW_STATUS_DEP_TIMEOUT) ? "dependency wait timed out" : "");
+    return PW_OK;
+}
+
+pw_status pw_plan_greedy(pw_layer L, const float* sensitivity, const float* residual,
+                         const int32_t* expert_count, int32_t n_tokens, const uint8_t* min_bits,
+                         const uint8_t* max_bits, double bytes_to_free, uint8_t* bits_out, double* result) {
+    g_err.clear();
+    if (!L || !sensitivity || !expert_count || !bits_out || !result)
+        return fail(PW_E_ARG, "pw_plan_greedy: null argument");
+    if (L->bits.empty()) return fail(PW_E_STATE, "pw_plan_greedy: the layer has no plan");
+    if (n_tokens <= 0) return fail(PW_E_ARG, "pw_plan_greedy: n_tokens %d", n_tokens);
+    if (!std::isfinite(bytes_to_free)) return fail(PW_E_ARG, "pw_plan_greedy: bytes_to_free not finite");
+    const pw_moe_desc& D = L->desc;
+    const int n = n_blocks(L), E = D.n_experts;
+    std::vector<int32_t> rows(n), cols(n);
+    std::vector<uint8_t> lo(n), hi(n);
+    std::vector<double> mass(n);
+    for (int e = 0; e < E; ++e)
+        if (expert_count[e] < 0) return fail(PW_E_ARG, "expert_count[%d] = %d", e, expert_count[e]);
+    for (int i = 0; i < n; ++i) {
+        const int e = i / 3, lin = i % 3;
+        if (!(sensitivity[i] >= 0.0f) || !std::isfinite(sensitivity[i]))
+            return fail(PW_E_ARG, "sensitivity[%d] must be finite and >= 0", i);
+        if (residual && (!(residual[i] >= 0.0f) || !std::isfinite(residual[i])))
+            return fail(PW_E_ARG, "residual[%d] must be finite and >= 0", i);
+        rows[i] = block_rows(L, e, lin);
+        cols[i] = block_cols(L, e, lin);
+        lo[i] = min_bits ? min_bits[i] : 3;
+        hi[i] = max_bits ? max_bits[i] : 8;
+        if (lo[i] < 1 || hi[i] > 8 || lo[i] > hi[i] || L->bits[i] < lo[i] || L->bits[i] > hi[i])
+            return fail(PW_E_BITS, "block %d: bits %d outside [%d, %d] (min/max in 1..8)", i, L->bits[i], lo[i], hi[i]);
+        mass[i] = e == E ? 1.0 : (double)expert_count[e] / (double)n_tokens;
+    }
+    pw::PlanProblem P{n, rows.data(), cols.data(), lo.data(), hi.data(), sensitivity, residual, mass.data()};
+    std::memcpy(bits_out, L->bits.data(), (size_t)n);
+    double moved = 0.0, dmg = 0.0;
+    const int actions = pw::plan_greedy(P, bytes_to_free, bits_out, &moved, &dmg);
+    result[0] = moved;
+    result[1] = dmg;
+    result[2] = actions;
     return PW_OK;
 }
 

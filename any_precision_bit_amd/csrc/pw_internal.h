@@ -97,6 +97,23 @@ struct ExpertParams {
     GemmParams dn;
 };
 
+// Planner problem: one entry per block (expert, linear), host arrays.
+struct PlanProblem {
+    int n_blocks;
+    const int32_t* rows;      // R of each block
+    const int32_t* cols;      // K of each block
+    const uint8_t* min_bits;  // floor of a downgrade
+    const uint8_t* max_bits;  // ceiling of an upgrade
+    const float* sens;        // offline sensitivity
+    const float* resid;       // prompt residual (may be null)
+    const double* mass;       // routing mass of the block's expert
+};
+// Resident bytes of an [R x K] block at bitwidth b: planes R*K*b/8 + LUT R*2^b*2.
+double block_bytes(int64_t R, int64_t K, int b);
+// Greedy plan change (see pw_plan.cpp); bits is updated in place. Returns the
+// number of actions; *moved = bytes released (> 0) or added (< 0).
+int plan_greedy(const PlanProblem& P, double bytes_to_free, uint8_t* bits, double* moved, double* damage);
+
 hipError_t launch_init_ws(const Workspace& ws, int n_counters, uint32_t wait_limit, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).

@@ -193,6 +193,37 @@ pw_status pw_moe_forward_noalloc(pw_layer layer, const void* x, int32_t T, const
                                  const void* router_b, float* y, void* x_next,
                                  const pw_route_out* route, void* stream);
 
+/* Quality-aware runtime planner (legiblepapers "Summary & Methodology Analysis"
+ * and FAQ Q8): from the layer's current plan, greedily choose one-bit
+ * bitwidth changes per block (expert, linear) until bytes_to_free bytes of
+ * pages are released, taking at each step the action with the least damage per
+ * released byte. bytes_to_free < 0 is a budget to spend instead: upgrades with
+ * the most benefit per added byte are taken while they fit. Host-only (no GPU
+ * call); the layer's plan is not changed: pass bits_out to pw_moe_plan_set and
+ * bind the pages it needs.
+ *   A block at bitwidth b holds R*K*b/8 + R*2^b*2 bytes (planes 0..b-1 and
+ *   LUT_b). The damage of b -> b-1 on block i of expert e is
+ *     (sensitivity[i] + residual[i]) * mass_e * (4^-(b-1) - 4^-b)
+ *   (quantisation noise power of a b-bit quantiser scales as 4^-b), with
+ *   mass_e = expert_count[e] / n_tokens for a routed expert (how often it is
+ *   used) and 1 for the shared expert. Ties go to the lower block index.
+ *   sensitivity  host float [n_blocks], finite, >= 0 (offline sensitivity)
+ *   residual     host float [n_blocks], finite, >= 0, or NULL (prompt residuals)
+ *   expert_count host int32 [n_experts] >= 0 (e.g. pw_route_out.expert_count of
+ *                a forward), n_tokens > 0 the tokens of that forward
+ *   min_bits / max_bits  host u8 [n_blocks] in 1..8 or NULL (3 and 8): no
+ *                downgrade below min, no upgrade above max; the current plan
+ *                must lie within them (PW_E_BITS otherwise)
+ *   bits_out     host u8 [n_blocks]: the new plan
+ *   result       host double [3]: bytes released (> 0) or added (< 0), damage
+ *                added (< 0 for upgrades: damage removed), number of actions
+ * A downgrade stops as soon as bytes_to_free is reached (it may overshoot by
+ * one action) or no action is left. PW_E_STATE without a plan. */
+pw_status pw_plan_greedy(pw_layer layer, const float* sensitivity, const float* residual,
+                         const int32_t* expert_count, int32_t n_tokens, const uint8_t* min_bits,
+                         const uint8_t* max_bits, double bytes_to_free, uint8_t* bits_out,
+                         double* result);
+
 /* Synchronises `stream`, then reads and clears the device status word into
  * *flags (PW_STATUS_* bits). Returns PW_E_STATE if any flag was set. */
 pw_status pw_layer_status(pw_layer layer, void* stream, uint32_t* flags);

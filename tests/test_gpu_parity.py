@@ -474,3 +474,46 @@ def test_abi_limits(torch_dev):
     x, wr, bias = layer_inputs(cfg)
     _say("ABI limits: d8192 E256 k16 max_tokens 65536")
     run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), max_tokens=65536)
+
+
+def test_planner_plan_forward(torch_dev):
+    """The planner's plan on the GPU: a qwen_d2048_t16 forward's routed counts feed pw_plan_greedy
+    (seeded synthetic sensitivities) with a target of 25 % of the resident bytes; the emitted plan
+    is set, its pages bound, and the next forward checked against the oracle on every token. Then
+    an upgrade with half of the freed bytes as budget, checked the same way."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import binding as B
+    from any_precision_bit_amd import route_buffers
+    from oracle import planner as OP
+
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    bits = synth.initial_bits(cfg)
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=tuple(range(3, 9))) for e, lin in jobs}
+    pages = device_pages(blocks, bits, dev, all_luts=True)
+    lay = gpu_layer(cfg, bits, pages, max_tokens=cfg.T)
+    x, wr, bias = layer_inputs(cfg)
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None, route=route)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy()
+    sens = np.random.default_rng(11).random(cfg.n_blocks).astype(np.float32)
+    shapes = OP.block_shapes(cfg.d, cfg.E, cfg.F, cfg.Fs)
+    resident = sum(OP.block_bytes(R, K, int(b)) for (R, K), b in zip(shapes, bits.reshape(-1)))
+    cur = bits
+    for step, tgt in (("downgrade", 0.25 * resident), ("upgrade", None)):
+        if tgt is None:
+            tgt = -0.5 * freed
+        new, moved, dmg, n = B.pw_plan_greedy(lay.handle, sens, counts, cfg.T, tgt)
+        ref = OP.plan(shapes, cur.reshape(-1), sens, OP.masses(cfg.E, True, counts, cfg.T), tgt)
+        assert np.array_equal(new, ref[0]) and n > 0
+        if step == "downgrade":
+            freed = moved
+            assert moved >= tgt
+        new = new.reshape(cur.shape)
+        lay.plan_set(new)
+        bind_all(lay, new, pages)
+        _say(f"planner {step}: {n} actions, {moved / 1e6:.1f} MB, mean bits {cur.mean():.2f} -> {new.mean():.2f}")
+        run_parity(torch_dev, cfg, new, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
+                   pages=pages)
+        cur = new
