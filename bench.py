@@ -277,6 +277,115 @@ def layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev, print_table=Tr
     return summary
 
 
+def paging_run(args, torch, synth, PagedMoELayer, dev, print_table=True):
+    """Asynchronous page movement on the qwen_d2048_t16 layer: forwards run back to back on the compute
+    stream, each bracketed by HIP events, first with no page movement, then while plan changes chosen
+    by the planner (a downgrade freeing 25 % of the resident bytes, then an upgrade back, repeated)
+    copy their pages host-to-device on a side stream; each change is committed as soon as its copies
+    have landed. Also times the planner itself on the host."""
+    from any_precision_bit_amd import binding as B
+    from any_precision_bit_amd import route_buffers
+    from any_precision_bit_amd.paging import PageManager
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    t0 = time.time()
+    bits = synth.initial_bits(cfg)
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=tuple(range(3, 9))) for e, lin in jobs}
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+    pm = PageManager(lay, {k: (b.planes, b.luts) for k, b in blocks.items()}, bits, dev)
+    del blocks
+    x, wr = f16(synth.tokens(cfg)), f16(synth.router(cfg)[0])
+    y = torch.empty((cfg.T, cfg.d), device=dev)
+    stream = pm.compute
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    lay.forward(x, wr, None, y=y, route=route, stream=stream)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy()
+    sens = np.random.default_rng(11).random(cfg.n_blocks).astype(np.float32)
+    log(f"paging: layer ready ({time.time() - t0:.1f}s), {pm.resident_bytes() / 1e6:.1f} MB resident")
+
+    # the planner on the host: one downgrade of 25 % of the resident bytes
+    resident = pm.resident_bytes()
+    reps = 200
+    tt = time.perf_counter()
+    for _ in range(reps):
+        down, moved, dmg, n_act = B.pw_plan_greedy(lay.handle, sens, counts, cfg.T, 0.25 * resident)
+    plan_us = (time.perf_counter() - tt) / reps * 1e6
+    # for comparison: the same bytes freed one random bit at a time (the seeded rewrite's style),
+    # scored with the planner's damage measure
+    g = np.random.default_rng(5)
+    cur = bits.reshape(-1).astype(int).copy()
+    shape = lambda i: ((cfg.Fs if i // 3 == cfg.E else cfg.F, cfg.d) if i % 3 < 2 else
+                       (cfg.d, cfg.Fs if i // 3 == cfg.E else cfg.F))
+    nbytes = lambda R, K, b: R * K * b / 8.0 + R * float(1 << b) * 2.0
+    mass = lambda i: 1.0 if i // 3 == cfg.E else counts[i // 3] / cfg.T
+    freed_r, dmg_r = 0.0, 0.0
+    while freed_r < 0.25 * resident:
+        i = int(g.integers(0, len(cur)))
+        if cur[i] <= 3:
+            continue
+        R, K = shape(i)
+        freed_r += nbytes(R, K, cur[i]) - nbytes(R, K, cur[i] - 1)
+        dmg_r += float(sens[i]) * mass(i) * (4.0 ** -(cur[i] - 1) - 4.0 ** -cur[i])
+        cur[i] -= 1
+
+    def run(n, changes):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        copied, copy_ms, overlapped, staged, plans, n_changes = 0, [], [], None, list(changes), 0
+        since = 0
+        for i in range(n):
+            if staged is None and plans:
+                staged = pm.stage(plans.pop(0))
+                since = 0
+            evs[i][0].record(stream)
+            lay.forward(x, wr, None, y=y, stream=stream)
+            evs[i][1].record(stream)
+            since += 1
+            if staged is not None and staged.ready():
+                pm.commit(staged)
+                copied += staged.nbytes
+                copy_ms.append(staged.copy_ms())
+                overlapped.append(since)
+                n_changes += 1
+                staged = None
+        if staged is not None:
+            pm.commit(staged)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        return us, copied, copy_ms, overlapped, n_changes
+
+    n = max(args.steps, 200)
+    for _ in range(args.warmup):
+        lay.forward(x, wr, None, y=y, stream=stream)
+    quiet, *_ = run(n, [])
+    cycle = [down.reshape(bits.shape), bits] * 8
+    moving, copied, copy_ms, overlapped, n_changes = run(n, cycle)
+    check_status([lay], "paging")
+    stat = lambda a: {"p50": round(float(np.percentile(a, 50)), 2), "p90": round(float(np.percentile(a, 90)), 2),
+                      "p99": round(float(np.percentile(a, 99)), 2), "max": round(float(a.max()), 2)}
+    out = {"workload": synth.WORKLOAD_TEXT["qwen_d2048_t16"], "forwards": n,
+           "forward_us_quiet": stat(quiet), "forward_us_while_moving": stat(moving),
+           "plan_changes_committed": n_changes, "copied_MB": round(copied / 1e6, 1),
+           "copy_ms_mean": round(float(np.mean(copy_ms)), 3) if copy_ms else None,
+           "copy_GBps": round(copied / 1e9 / (np.sum(copy_ms) * 1e-3), 1) if copy_ms else None,
+           "forwards_overlapped_per_change": round(float(np.mean(overlapped)), 1) if overlapped else None,
+           "planner": {"host_us": round(plan_us, 1), "blocks": cfg.n_blocks, "target_MB": round(0.25 * resident / 1e6, 1),
+                       "freed_MB": round(moved / 1e6, 1), "actions": n_act, "damage": dmg,
+                       "damage_random_same_bytes": dmg_r, "freed_random_MB": round(freed_r / 1e6, 1)},
+           "status_checked": True}
+    if print_table:
+        print(json.dumps(out, indent=1))
+    lay.close()
+    del pm
+    torch.cuda.empty_cache()
+    return out
+
+
 def check_status(lays, what):
     """Reads (and clears) the device status word of every layer; a set flag means a forward's output
     was not valid (router range, or a dependency wait that gave up), so no figure is published."""
@@ -372,6 +481,8 @@ def main():
                     help="with --sweep: time only the workload of this label (e.g. 'mixtral_d4096 T=64')")
     ap.add_argument("--stack", action="store_true",
                     help="time the 24-layer qwen_stack24_t256 workload over 64 steps with plan rewrites")
+    ap.add_argument("--paging", action="store_true",
+                    help="forward latency with and without asynchronous page movement, and the planner's host time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -402,6 +513,9 @@ def main():
         return
     if args.stack:
         layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev)
+        return
+    if args.paging:
+        paging_run(args, torch, synth, PagedMoELayer, dev)
         return
     cfg = synth.CONFIGS["qwen_d2048_t16"]
     T = cfg.T
@@ -491,6 +605,11 @@ def main():
         log(f"mixtral_d4096 T=1: median {med:.1f} us")
         subs["qwen_stack24_t256"] = layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev, print_table=False)
         log(f"qwen_stack24_t256: {subs['qwen_stack24_t256']['value']:,.0f} tokens/s")
+        subs["page_movement"] = paging_run(args, torch, synth, PagedMoELayer, dev, print_table=False)
+        pg = subs["page_movement"]
+        log(f"page movement: forward p50 {pg['forward_us_quiet']['p50']} -> {pg['forward_us_while_moving']['p50']} us, "
+            f"p99 {pg['forward_us_quiet']['p99']} -> {pg['forward_us_while_moving']['p99']} us, "
+            f"{pg['copied_MB']} MB at {pg['copy_GBps']} GB/s; planner {pg['planner']['host_us']} us")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -517,3 +517,47 @@ def test_planner_plan_forward(torch_dev):
         run_parity(torch_dev, cfg, new, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
                    pages=pages)
         cur = new
+
+
+def test_async_page_movement(torch_dev):
+    """Asynchronous page movement on qwen_d2048_t16: pages of a planner downgrade (25 % of the
+    resident bytes) and then of an upgrade back are copied on a side stream while forwards keep
+    running on the compute stream with the old plan; after each commit the device holds exactly the
+    pages the plan reads, and the next forward matches the oracle on every token."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import PagedMoELayer, route_buffers
+    from any_precision_bit_amd import binding as B
+    from any_precision_bit_amd.paging import PageManager
+    from oracle import planner as OP
+
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    bits = synth.initial_bits(cfg)
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=tuple(range(3, 9))) for e, lin in jobs}
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+    pm = PageManager(lay, {k: (b.planes, b.luts) for k, b in blocks.items()}, bits, dev)
+    shapes = OP.block_shapes(cfg.d, cfg.E, cfg.F, cfg.Fs)
+    plan_bytes = lambda bb: sum(OP.block_bytes(R, K, int(b)) for (R, K), b in zip(shapes, np.asarray(bb).reshape(-1)))
+    assert pm.resident_bytes() == plan_bytes(bits)
+    x, wr, bias = layer_inputs(cfg)
+    xd, wd = to_dev_f16(x, dev), to_dev_f16(wr, dev)
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    lay.forward(xd, wd, None, route=route)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy()
+    sens = np.random.default_rng(11).random(cfg.n_blocks).astype(np.float32)
+    cur = bits
+    for step in ("downgrade", "upgrade"):
+        tgt = 0.25 * plan_bytes(cur) if step == "downgrade" else -0.25 * plan_bytes(bits)
+        new, moved, _, n = B.pw_plan_greedy(lay.handle, sens, counts, cfg.T, tgt, max_bits=np.full(cfg.n_blocks, 8, np.uint8))
+        staged = pm.stage(new)
+        y = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=dev)
+        for _ in range(8):                      # forwards with the old plan while the copies run
+            lay.forward(xd, wd, None, y=y)
+        pm.commit(staged)
+        _say(f"paging {step}: {n} actions, {staged.nbytes / 1e6:.1f} MB copied in {staged.copy_ms():.2f} ms")
+        torch.cuda.synchronize()
+        cur = new.reshape(cur.shape)
+        assert pm.resident_bytes() == plan_bytes(cur)
+        run_parity(torch_dev, cfg, cur, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
+                   pages=pm.dev)
