@@ -386,6 +386,89 @@ def paging_run(args, torch, synth, PagedMoELayer, dev, print_table=True):
     return out
 
 
+def kv_pressure_run(args, torch, synth, PagedMoELayer, dev, print_table=True):
+    """KV-cache pressure driving the planner on the qwen_d2048_t16 layer: one forward per decode step of
+    a seeded request trace (the forward's batch stays the workload's 16 tokens; the trace sets the
+    layer's share of KV bytes, 16 KV heads x 128 x fp16 per token). The memory budget is the starting
+    plan's page bytes plus the trace's median KV bytes; every 8 steps the byte target (resident pages
+    + KV - budget) is passed to the planner, the plan's pages move on a side stream and are committed
+    when they have landed. Reports weight bytes, plan changes, damage, the worst overshoot of the
+    budget, and forward latency."""
+    from any_precision_bit_amd import route_buffers
+    from any_precision_bit_amd.kvpressure import KVPressurePlanner
+    from any_precision_bit_amd.paging import PageManager
+    from synth.kvtrace import kv_bytes_per_token, request_trace
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    bits = synth.initial_bits(cfg)
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=tuple(range(3, 9))) for e, lin in jobs}
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+    pm = PageManager(lay, {k: (b.planes, b.luts) for k, b in blocks.items()}, bits, dev)
+    del blocks
+    x, wr = f16(synth.tokens(cfg)), f16(synth.router(cfg)[0])
+    y = torch.empty((cfg.T, cfg.d), device=dev)
+    stream = pm.compute
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    lay.forward(x, wr, None, y=y, route=route, stream=stream)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy()
+    steps = 800
+    # a request rate whose KV swing (about 0.3 GB) is what one layer's plan can absorb
+    kv = request_trace(steps, seed=3, peak_rate=0.12).astype(np.float64) * kv_bytes_per_token(1, 16, 128)
+    w0 = float(pm.resident_bytes())
+    budget = w0 + float(np.median(kv))
+    sens = np.random.default_rng(11).random(cfg.n_blocks).astype(np.float32)
+    ctl = KVPressurePlanner(lay, budget, sens, hysteresis_bytes=0.02 * w0, resident_bytes=pm.resident_bytes,
+                            max_bits=bits.reshape(-1))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    staged, n_down, n_up, moved_total, damage, over, wmin, wmax = None, 0, 0, 0.0, 0.0, 0.0, w0, w0
+    for s_ in range(steps):
+        if staged is None and s_ % 8 == 0:
+            d = ctl.decide(kv[s_], counts, cfg.T)
+            if d is not None:
+                staged = pm.stage(d[0].reshape(bits.shape))
+                moved_total += abs(d[1])
+                damage += max(d[2], 0.0)
+                n_down += d[1] > 0
+                n_up += d[1] < 0
+        evs[s_][0].record(stream)
+        lay.forward(x, wr, None, y=y, stream=stream)
+        evs[s_][1].record(stream)
+        if staged is not None and staged.ready():
+            pm.commit(staged)
+            staged = None
+        w = float(pm.resident_bytes())
+        wmin, wmax = min(wmin, w), max(wmax, w)
+        over = max(over, w + kv[s_] - budget)
+    if staged is not None:
+        pm.commit(staged)
+    torch.cuda.synchronize()
+    check_status([lay], "kv pressure")
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    out = {"workload": synth.WORKLOAD_TEXT["qwen_d2048_t16"], "steps": steps,
+           "kv_MB": {"min": round(kv.min() / 1e6, 1), "median": round(float(np.median(kv)) / 1e6, 1),
+                     "max": round(kv.max() / 1e6, 1)},
+           "budget_MB": round(budget / 1e6, 1), "weights_MB": {"start": round(w0 / 1e6, 1), "min": round(wmin / 1e6, 1),
+                                                               "max": round(wmax / 1e6, 1)},
+           "plan_changes": {"down": int(n_down), "up": int(n_up)}, "moved_MB": round(moved_total / 1e6, 1),
+           "downgrade_damage_sum": damage, "final_bits_equal_start": bool((pm.bits == bits).all()),
+           "worst_overshoot_MB": round(over / 1e6, 1),
+           "forward_us": {"p50": round(float(np.percentile(us, 50)), 2), "p99": round(float(np.percentile(us, 99)), 2),
+                          "max": round(float(us.max()), 2)},
+           "tokens_per_s": round(cfg.T * steps / (us.sum() * 1e-6), 1), "status_checked": True}
+    if print_table:
+        print(json.dumps(out, indent=1))
+    lay.close()
+    del pm
+    torch.cuda.empty_cache()
+    return out
+
+
 def check_status(lays, what):
     """Reads (and clears) the device status word of every layer; a set flag means a forward's output
     was not valid (router range, or a dependency wait that gave up), so no figure is published."""
@@ -483,6 +566,8 @@ def main():
                     help="time the 24-layer qwen_stack24_t256 workload over 64 steps with plan rewrites")
     ap.add_argument("--paging", action="store_true",
                     help="forward latency with and without asynchronous page movement, and the planner's host time")
+    ap.add_argument("--kv-pressure", action="store_true",
+                    help="a seeded KV-cache trace driving the planner and page movement on the decode layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -516,6 +601,9 @@ def main():
         return
     if args.paging:
         paging_run(args, torch, synth, PagedMoELayer, dev)
+        return
+    if args.kv_pressure:
+        kv_pressure_run(args, torch, synth, PagedMoELayer, dev)
         return
     cfg = synth.CONFIGS["qwen_d2048_t16"]
     T = cfg.T
@@ -610,6 +698,10 @@ def main():
         log(f"page movement: forward p50 {pg['forward_us_quiet']['p50']} -> {pg['forward_us_while_moving']['p50']} us, "
             f"p99 {pg['forward_us_quiet']['p99']} -> {pg['forward_us_while_moving']['p99']} us, "
             f"{pg['copied_MB']} MB at {pg['copy_GBps']} GB/s; planner {pg['planner']['host_us']} us")
+        subs["kv_pressure"] = kv_pressure_run(args, torch, synth, PagedMoELayer, dev, print_table=False)
+        kp = subs["kv_pressure"]
+        log(f"kv pressure: {kp['plan_changes']} plan changes, weights {kp['weights_MB']} MB, "
+            f"worst overshoot {kp['worst_overshoot_MB']} MB")
 
     cpu = None
     if not args.no_cpu_baseline:

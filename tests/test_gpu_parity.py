@@ -561,3 +561,45 @@ def test_async_page_movement(torch_dev):
         assert pm.resident_bytes() == plan_bytes(cur)
         run_parity(torch_dev, cfg, cur, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
                    pages=pm.dev)
+
+
+def test_kv_pressure_plans(torch_dev):
+    """KV-cache pressure driving the planner through the page manager on qwen_d2048_t16: KV bytes
+    rising past the budget force downgrades (weights + KV back within the budget), falling KV allows
+    upgrades back toward the starting plan; after every committed change the layer matches the
+    oracle on every token."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import PagedMoELayer, route_buffers
+    from any_precision_bit_amd.kvpressure import KVPressurePlanner
+    from any_precision_bit_amd.paging import PageManager
+
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    bits = synth.initial_bits(cfg)
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=tuple(range(3, 9))) for e, lin in jobs}
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T)
+    pm = PageManager(lay, {k: (b.planes, b.luts) for k, b in blocks.items()}, bits, dev)
+    x, wr, bias = layer_inputs(cfg)
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None, route=route)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy()
+    w0 = float(pm.resident_bytes())
+    budget = w0 + 100e6
+    ctl = KVPressurePlanner(lay, budget, np.random.default_rng(4).random(cfg.n_blocks).astype(np.float32),
+                            hysteresis_bytes=5e6, resident_bytes=pm.resident_bytes, max_bits=bits.reshape(-1))
+    seen = set()
+    for kv in (50e6, 160e6, 220e6, 120e6, 20e6):
+        d = ctl.decide(kv, counts, cfg.T)
+        if d is None:
+            continue
+        staged = pm.stage(d[0].reshape(bits.shape))
+        pm.commit(staged)
+        torch.cuda.synchronize()
+        seen.add("down" if d[1] > 0 else "up")
+        if d[1] > 0:
+            assert pm.resident_bytes() + kv <= budget
+        _say(f"kv {kv / 1e6:.0f} MB: {d[3]} actions, weights {pm.resident_bytes() / 1e6:.1f} MB")
+        run_parity(torch_dev, cfg, pm.bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
+                   pages=pm.dev)
+    assert seen == {"down", "up"}
