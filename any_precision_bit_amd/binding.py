@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
             "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
             "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit",
-            "pw_moe_forward_noalloc", "pw_plan_greedy"]
+            "pw_moe_forward_noalloc", "pw_plan_greedy", "pw_page_table_bind_rows"]
 
 
 class PwError(RuntimeError):
@@ -37,7 +37,7 @@ class pw_moe_desc(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("d_ffn", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_ffn_shared", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("rows_per_block", ctypes.c_int32)]
 
 
 class pw_route_out(ctypes.Structure):
@@ -65,6 +65,7 @@ def _load():
         "pw_last_error": ([], ctypes.c_char_p),
         "pw_moe_plan_set": ([P, P, i32], st),
         "pw_page_table_bind": ([P, i32, i32, P, i32, P, i32], st),
+        "pw_page_table_bind_rows": ([P, i32, i32, i32, P, i32, P, i32], st),
         "pw_moe_forward": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_moe_forward_noalloc": ([P, P, i32, P, P, P, P, ctypes.POINTER(pw_route_out), P], st),
         "pw_layer_status": ([P, P, ctypes.POINTER(u32)], st),
@@ -95,8 +96,9 @@ def _check(status: int):
 
 
 def pw_layer_create(d_model, n_experts, d_ffn, top_k, d_ffn_shared, max_tokens, flags=0,
-                    abi_version=PW_ABI_VERSION) -> int:
-    desc = pw_moe_desc(abi_version, d_model, n_experts, d_ffn, top_k, d_ffn_shared, max_tokens, flags)
+                    abi_version=PW_ABI_VERSION, rows_per_block=0) -> int:
+    desc = pw_moe_desc(abi_version, d_model, n_experts, d_ffn, top_k, d_ffn_shared, max_tokens, flags,
+                       rows_per_block)
     out = ctypes.c_void_p()
     _check(lib.pw_layer_create(ctypes.byref(desc), ctypes.byref(out)))
     return out.value
@@ -117,6 +119,13 @@ def pw_page_table_bind(layer: int, expert: int, linear: int, planes, lut: int, l
     """planes: sequence of device addresses (ints) of planes 0..n-1."""
     arr = (ctypes.c_void_p * max(1, len(planes)))(*[int(p) for p in planes])
     _check(lib.pw_page_table_bind(layer, expert, linear, arr, len(planes), lut, lut_bits))
+
+
+def pw_page_table_bind_rows(layer: int, expert: int, linear: int, row_block: int, planes, lut: int,
+                            lut_bits: int) -> None:
+    """planes: sequence of device addresses (ints) of the block's rows of planes 0..n-1."""
+    arr = (ctypes.c_void_p * max(1, len(planes)))(*[int(p) for p in planes])
+    _check(lib.pw_page_table_bind_rows(layer, expert, linear, row_block, arr, len(planes), lut, lut_bits))
 
 
 def pw_moe_forward(layer: int, x: int, T: int, router_w: int, router_b, y: int, x_next=None,

@@ -117,19 +117,38 @@ struct pw_layer_s {
     // host copy of the page table for pw_moe_forward_noalloc (sized at create)
     std::vector<DevBlock> shadow;
     uint32_t* noalloc_status = nullptr;   // status word in the device scratch, once used
+    // blocks in order (expert, linear, row-block): expert, linear, rows, columns, first block of
+    // each (expert, linear)
+    std::vector<int32_t> blk_expert, blk_lin, blk_rows, blk_cols, first_block;
 };
 
 namespace {
 
-int n_blocks(const pw_layer_s* L) { return L->n_total * 3; }
+int n_blocks(const pw_layer_s* L) { return (int)L->blk_rows.size(); }
 
-int block_rows(const pw_layer_s* L, int e, int lin) {
+int linear_rows(const pw_layer_s* L, int e, int lin) {
     const int f = (e == L->desc.n_experts) ? L->desc.d_ffn_shared : L->desc.d_ffn;
     return lin == PW_DOWN ? L->desc.d_model : f;
 }
-int block_cols(const pw_layer_s* L, int e, int lin) {
+int linear_cols(const pw_layer_s* L, int e, int lin) {
     const int f = (e == L->desc.n_experts) ? L->desc.d_ffn_shared : L->desc.d_ffn;
     return lin == PW_DOWN ? f : L->desc.d_model;
+}
+
+// The layer's blocks: every linear whole (rows_per_block 0) or cut into row-blocks.
+void make_block_list(pw_layer_s* L) {
+    const int rb = L->desc.rows_per_block;
+    for (int e = 0; e < L->n_total; ++e)
+        for (int lin = 0; lin < 3; ++lin) {
+            const int R = linear_rows(L, e, lin), rows = rb ? rb : R;
+            L->first_block.push_back((int32_t)L->blk_rows.size());
+            for (int j = 0; j < R / rows; ++j) {
+                L->blk_expert.push_back(e);
+                L->blk_lin.push_back(lin);
+                L->blk_rows.push_back(rows);
+                L->blk_cols.push_back(linear_cols(L, e, lin));
+            }
+        }
 }
 
 // Checks that every block's pages cover its planned bitwidth.
@@ -140,8 +159,9 @@ pw_status validate_tables(const pw_layer_s* L) {
         const Page& pg = L->pages[i];
         if (pg.n_planes < b || pg.lut_bits != b || pg.lut == nullptr)
             return fail(PW_E_UNBOUND,
-                        "block (expert %d, linear %d): planned b=%d but bound %d planes and LUT bits %d",
-                        i / 3, i % 3, b, pg.n_planes, pg.lut_bits);
+                        "block %d (expert %d, linear %d, row-block %d): planned b=%d but bound %d planes and LUT bits %d",
+                        i, L->blk_expert[i], L->blk_lin[i], i - L->first_block[L->blk_expert[i] * 3 + L->blk_lin[i]],
+                        b, pg.n_planes, pg.lut_bits);
     }
     return PW_OK;
 }
@@ -347,6 +367,7 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     gp.ld_act = f_max;
     gp.shared_base = shared_base;
     gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
+    gp.rb = D.rows_per_block;
     gp.y = y;
     // gate_up + SwiGLU: items of 32 rows of F (gate and up)
     r.gu = gp;
@@ -450,6 +471,11 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     if (D.abi_version != PW_ABI_VERSION)
         return fail(PW_E_ARG, "abi_version %d, library is %d", D.abi_version, PW_ABI_VERSION);
     if (D.flags & ~PW_FLAG_LUT_TILED) return fail(PW_E_ARG, "flags 0x%x: only PW_FLAG_LUT_TILED is defined", D.flags);
+    if (D.rows_per_block < 0 || D.rows_per_block % 64 ||
+        (D.rows_per_block > 0 && (D.d_model % D.rows_per_block || D.d_ffn % D.rows_per_block ||
+                                  D.d_ffn_shared % D.rows_per_block)))
+        return fail(PW_E_SHAPE, "rows_per_block %d: must be 0 or a multiple of 64 dividing d_model, d_ffn and "
+                    "d_ffn_shared", D.rows_per_block);
     if (D.d_model <= 0 || D.d_model % 128 || D.d_model > pw::kMaxModel)
         return fail(PW_E_SHAPE, "d_model %d: must be a positive multiple of 128, at most %d", D.d_model,
                     pw::kMaxModel);
@@ -472,6 +498,7 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     if (!L) return fail(PW_E_NOMEM, "pw_layer_create: out of host memory");
     L->desc = D;
     L->n_total = D.n_experts + (D.d_ffn_shared > 0 ? 1 : 0);
+    make_block_list(L);
     L->pages.resize((size_t)n_blocks(L));
     L->shadow.resize((size_t)n_blocks(L));
     int dev = 0;
@@ -499,11 +526,33 @@ pw_status pw_moe_plan_set(pw_layer L, const uint8_t* bits, int32_t n) {
         return fail(PW_E_ARG, "pw_moe_plan_set: n_blocks %d, layer has %d", n, n_blocks(L));
     for (int i = 0; i < n; ++i)
         if (bits[i] < 1 || bits[i] > PW_MAX_BITS)
-            return fail(PW_E_BITS, "block %d (expert %d, linear %d): bits %d not in 1..8", i, i / 3, i % 3,
-                        bits[i]);
+            return fail(PW_E_BITS, "block %d (expert %d, linear %d): bits %d not in 1..8", i, L->blk_expert[i],
+                        L->blk_lin[i], bits[i]);
     L->bits.assign(bits, bits + n);
     L->dirty = true;
     return PW_OK;
+}
+
+// Checks the pages of one bind; the caller has checked the layer and the block.
+pw_status check_pages(const void* const* planes, int32_t n_planes, const void* lut, int32_t lut_bits) {
+    if (n_planes < 1 || n_planes > 8) return fail(PW_E_ARG, "n_planes %d not in 1..8", n_planes);
+    if (lut_bits < 1 || lut_bits > PW_MAX_BITS) return fail(PW_E_BITS, "lut_bits %d not in 1..8", lut_bits);
+    if (!planes || !lut) return fail(PW_E_ARG, "pw_page_table_bind: null planes or lut");
+    for (int p = 0; p < n_planes; ++p) {
+        if (!planes[p]) return fail(PW_E_ARG, "plane %d is null", p);
+        if (!aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d is not 16-byte aligned", p);
+    }
+    if (!aligned16(lut)) return fail(PW_E_ALIGN, "lut is not 16-byte aligned");
+    return PW_OK;
+}
+
+void set_page(pw_layer_s* L, int block, const void* const* planes, int32_t n_planes, size_t plane_off,
+              const void* lut, int32_t lut_bits, size_t lut_off) {
+    Page& pg = L->pages[(size_t)block];
+    for (int p = 0; p < 8; ++p) pg.planes[p] = p < n_planes ? (const char*)planes[p] + plane_off : nullptr;
+    pg.n_planes = n_planes;
+    pg.lut = (const char*)lut + lut_off;
+    pg.lut_bits = lut_bits;
 }
 
 pw_status pw_page_table_bind(pw_layer L, int32_t expert, int32_t linear, const void* const* planes,
@@ -513,19 +562,32 @@ pw_status pw_page_table_bind(pw_layer L, int32_t expert, int32_t linear, const v
     if (expert < 0 || expert >= L->n_total)
         return fail(PW_E_ARG, "expert %d not in 0..%d", expert, L->n_total - 1);
     if (linear < PW_GATE || linear > PW_DOWN) return fail(PW_E_ARG, "linear %d not in 0..2", linear);
-    if (n_planes < 1 || n_planes > 8) return fail(PW_E_ARG, "n_planes %d not in 1..8", n_planes);
-    if (lut_bits < 1 || lut_bits > PW_MAX_BITS) return fail(PW_E_BITS, "lut_bits %d not in 1..8", lut_bits);
-    if (!planes || !lut) return fail(PW_E_ARG, "pw_page_table_bind: null planes or lut");
-    for (int p = 0; p < n_planes; ++p) {
-        if (!planes[p]) return fail(PW_E_ARG, "plane %d is null", p);
-        if (!aligned16(planes[p])) return fail(PW_E_ALIGN, "plane %d is not 16-byte aligned", p);
-    }
-    if (!aligned16(lut)) return fail(PW_E_ALIGN, "lut is not 16-byte aligned");
-    Page& pg = L->pages[(size_t)expert * 3 + linear];
-    for (int p = 0; p < 8; ++p) pg.planes[p] = p < n_planes ? planes[p] : nullptr;
-    pg.n_planes = n_planes;
-    pg.lut = lut;
-    pg.lut_bits = lut_bits;
+    pw_status st = check_pages(planes, n_planes, lut, lut_bits);
+    if (st != PW_OK) return st;
+    // every row-block of the linear, from whole-linear pages: row-block j starts j*rows rows in
+    const int first = L->first_block[expert * 3 + linear];
+    const int R = linear_rows(L, expert, linear), rows = L->blk_rows[first], K = L->blk_cols[first];
+    for (int j = 0; j < R / rows; ++j)
+        set_page(L, first + j, planes, n_planes, (size_t)j * rows * (K / 8), lut, lut_bits,
+                 (size_t)j * rows * ((size_t)1 << lut_bits) * 2);
+    L->dirty = true;
+    return PW_OK;
+}
+
+pw_status pw_page_table_bind_rows(pw_layer L, int32_t expert, int32_t linear, int32_t row_block,
+                                  const void* const* planes, int32_t n_planes, const void* lut, int32_t lut_bits) {
+    g_err.clear();
+    if (!L) return fail(PW_E_ARG, "pw_page_table_bind_rows: null layer");
+    if (expert < 0 || expert >= L->n_total)
+        return fail(PW_E_ARG, "expert %d not in 0..%d", expert, L->n_total - 1);
+    if (linear < PW_GATE || linear > PW_DOWN) return fail(PW_E_ARG, "linear %d not in 0..2", linear);
+    const int first = L->first_block[expert * 3 + linear];
+    const int n_rb = linear_rows(L, expert, linear) / L->blk_rows[first];
+    if (row_block < 0 || row_block >= n_rb)
+        return fail(PW_E_ARG, "row_block %d not in 0..%d", row_block, n_rb - 1);
+    pw_status st = check_pages(planes, n_planes, lut, lut_bits);
+    if (st != PW_OK) return st;
+    set_page(L, first + row_block, planes, n_planes, 0, lut, lut_bits, 0);
     L->dirty = true;
     return PW_OK;
 }
@@ -653,13 +715,13 @@ pw_status pw_plan_greedy(pw_layer L, const float* sensitivity, const float* resi
     for (int e = 0; e < E; ++e)
         if (expert_count[e] < 0) return fail(PW_E_ARG, "expert_count[%d] = %d", e, expert_count[e]);
     for (int i = 0; i < n; ++i) {
-        const int e = i / 3, lin = i % 3;
+        const int e = L->blk_expert[i];
         if (!(sensitivity[i] >= 0.0f) || !std::isfinite(sensitivity[i]))
             return fail(PW_E_ARG, "sensitivity[%d] must be finite and >= 0", i);
         if (residual && (!(residual[i] >= 0.0f) || !std::isfinite(residual[i])))
             return fail(PW_E_ARG, "residual[%d] must be finite and >= 0", i);
-        rows[i] = block_rows(L, e, lin);
-        cols[i] = block_cols(L, e, lin);
+        rows[i] = L->blk_rows[i];
+        cols[i] = L->blk_cols[i];
         lo[i] = min_bits ? min_bits[i] : 3;
         hi[i] = max_bits ? max_bits[i] : 8;
         if (lo[i] < 1 || hi[i] > 8 || lo[i] > hi[i] || L->bits[i] < lo[i] || L->bits[i] > hi[i])
@@ -690,17 +752,14 @@ pw_status pw_layer_last_bytes(pw_layer L, void* stream, double* bytes) {
         hipSuccess)
         return hip_fail(e, "counts read");
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "counts sync");
-    auto blk_bytes = [&](int ex, int lin) {
-        const int b = L->bits[(size_t)ex * 3 + lin];
-        const double R = block_rows(L, ex, lin), K = block_cols(L, ex, lin);
-        return R * K * b / 8.0 + R * (double)(1 << b) * 2.0;
-    };
     double gu = 0, dn = 0;
-    for (int ex = 0; ex < L->n_total; ++ex) {
-        const bool active = (ex == E) || cnt[ex] > 0;
-        if (!active) continue;
-        gu += blk_bytes(ex, PW_GATE) + blk_bytes(ex, PW_UP);
-        dn += blk_bytes(ex, PW_DOWN);
+    for (int i = 0; i < n_blocks(L); ++i) {
+        const int ex = L->blk_expert[i];
+        if (ex != E && cnt[ex] == 0) continue;   // experts without tokens read nothing
+        const int b = L->bits[i];
+        const double R = L->blk_rows[i], K = L->blk_cols[i];
+        const double bytes = R * K * b / 8.0 + R * (double)(1 << b) * 2.0;
+        (L->blk_lin[i] == PW_DOWN ? dn : gu) += bytes;
     }
     bytes[0] = (double)T * d * 2 + (double)E * d * 2;   // x and router weights read
     bytes[1] = gu + (double)T * d * 2;                  // gate/up pages + x

@@ -20,13 +20,16 @@ class PagedMoELayer:
     bound pages so they outlive the forwards that read them."""
 
     def __init__(self, d_model: int, n_experts: int, d_ffn: int, top_k: int,
-                 d_ffn_shared: int = 0, max_tokens: int = 256, lut_tiled: bool = False):
+                 d_ffn_shared: int = 0, max_tokens: int = 256, lut_tiled: bool = False,
+                 rows_per_block: int = 0):
         self.d_model, self.n_experts, self.d_ffn = d_model, n_experts, d_ffn
         self.top_k, self.d_ffn_shared, self.max_tokens = top_k, d_ffn_shared, max_tokens
         self.n_total = n_experts + (1 if d_ffn_shared > 0 else 0)
         self.lut_tiled = lut_tiled
+        self.rows_per_block = rows_per_block
         self.handle = B.pw_layer_create(d_model, n_experts, d_ffn, top_k, d_ffn_shared, max_tokens,
-                                        flags=B.PW_FLAG_LUT_TILED if lut_tiled else 0)
+                                        flags=B.PW_FLAG_LUT_TILED if lut_tiled else 0,
+                                        rows_per_block=rows_per_block)
         self._pages = {}
 
     def close(self):
@@ -53,6 +56,13 @@ class PagedMoELayer:
             addrs = [int(p.data_ptr()) for p in planes]
         B.pw_page_table_bind(self.handle, expert, linear, addrs, int(lut.data_ptr()), lut_bits)
         self._pages[(expert, linear)] = (planes, lut)
+
+    def bind_rows(self, expert: int, linear: int, row_block: int, planes: Sequence[torch.Tensor],
+                  lut: torch.Tensor, lut_bits: int) -> None:
+        """Pages of one row-block: per-plane tensors of its rows and its rows of the LUT."""
+        B.pw_page_table_bind_rows(self.handle, expert, linear, row_block, [int(p.data_ptr()) for p in planes],
+                                  int(lut.data_ptr()), lut_bits)
+        self._pages[(expert, linear, row_block)] = (planes, lut)
 
     def forward(self, x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, x_next: Optional[torch.Tensor] = None,

@@ -469,6 +469,73 @@ def kv_pressure_run(args, torch, synth, PagedMoELayer, dev, print_table=True):
     return out
 
 
+def prefill_run(args, torch, synth, PagedMoELayer, dev, print_table=True):
+    """The T = 1024 prefill workload with linear-blocks of 128 rows (qwen_rows128_t1024): every
+    block at its own bitwidth, bound block by block; per-call times of whole forwards over two
+    byte-identical page clones, HIP events on the launch stream. Useful MFMA work counts
+    2 * tokens * rows * K of every block over the tokens routed to its expert."""
+    from any_precision_bit_amd import route_buffers
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float16).view(np.int16).copy()).to(dev).view(
+            torch.float16)
+
+    cfg = synth.CONFIGS["qwen_rows128_t1024"]
+    rb = synth.ROWS_PER_BLOCK[cfg.name]
+    bits = synth.rowblock_bits(cfg, rb)
+    t0 = time.time()
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    base = {}
+    for e, lin in jobs:
+        blk = synth.make_block(cfg, e, lin, n_planes=8, lut_bits=(3, 4, 5, 6, 8))
+        base[(e, lin)] = (torch.from_numpy(np.ascontiguousarray(blk.planes)).to(dev),
+                          {b: f16(v) for b, v in blk.luts.items()})
+    lays = []
+    for c in range(2):
+        pages = base if c == 0 else {k: (p.clone(), {b: l.clone() for b, l in ls.items()}) for k, (p, ls) in base.items()}
+        lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T, rows_per_block=rb)
+        lay.plan_set(bits)
+        i = 0
+        for e, lin in jobs:
+            planes, luts = pages[(e, lin)]
+            for j in range(planes.shape[1] // rb):
+                b = int(bits[i])
+                i += 1
+                rows = slice(j * rb, (j + 1) * rb)
+                lay.bind_rows(e, lin, j, [planes[p][rows] for p in range(b)], luts[b][rows], b)
+        lays.append(dict(lay=lay, pages=pages, x=f16(synth.tokens(cfg)), wr=f16(synth.router(cfg)[0]), bias=None,
+                         y=torch.empty((cfg.T, cfg.d), device=dev)))
+    torch.cuda.synchronize()
+    log(f"qwen_rows128_t1024: pages ready ({time.time() - t0:.1f}s)")
+    stream = torch.cuda.current_stream(dev)
+    us = time_per_call(torch, lays, stream, 40, 4)
+    check_status([c["lay"] for c in lays], "qwen_rows128_t1024")
+    nb = lays[0]["lay"].last_bytes(stream)
+    layer_bytes = nb[0] + nb[1] + nb[2]
+    route = route_buffers(cfg.T, cfg.E, cfg.k, dev)
+    c0 = lays[0]
+    c0["lay"].forward(c0["x"], c0["wr"], None, y=c0["y"], route=route, stream=stream)
+    torch.cuda.synchronize()
+    counts = route["expert_count"].cpu().numpy().astype(np.float64)
+    flops = 2.0 * 3 * cfg.F * cfg.d * counts.sum() + 2.0 * 3 * cfg.Fs * cfg.d * cfg.T
+    med = float(np.median(us))
+    out = {"workload": synth.WORKLOAD_TEXT[cfg.name], "tokens": cfg.T, "rows_per_block": rb,
+           "blocks": int(bits.shape[0]), "mean_bits": round(float(bits.mean()), 3), "value": round(cfg.T / (med * 1e-6), 1),
+           "unit": "tokens/s", "us_median": round(med, 1), "us_p10": round(float(np.percentile(us, 10)), 1),
+           "us_p90": round(float(np.percentile(us, 90)), 1), "layer_bytes": layer_bytes,
+           "layer_hbm_frac": round(layer_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "useful_mfma_TFLOPs": round(flops / (med * 1e-6) / 1e12, 1),
+           "mfma_frac_of_fp16_peak": round(flops / (med * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+           "rotation_clones": 2, "status_checked": True}
+    if print_table:
+        print(json.dumps(out, indent=1))
+    for c in lays:
+        c["lay"].close()
+    del lays, base
+    torch.cuda.empty_cache()
+    return out
+
+
 def check_status(lays, what):
     """Reads (and clears) the device status word of every layer; a set flag means a forward's output
     was not valid (router range, or a dependency wait that gave up), so no figure is published."""
@@ -566,6 +633,8 @@ def main():
                     help="time the 24-layer qwen_stack24_t256 workload over 64 steps with plan rewrites")
     ap.add_argument("--paging", action="store_true",
                     help="forward latency with and without asynchronous page movement, and the planner's host time")
+    ap.add_argument("--prefill", action="store_true",
+                    help="the T = 1024 prefill workload with 128-row linear-blocks")
     ap.add_argument("--kv-pressure", action="store_true",
                     help="a seeded KV-cache trace driving the planner and page movement on the decode layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -604,6 +673,9 @@ def main():
         return
     if args.kv_pressure:
         kv_pressure_run(args, torch, synth, PagedMoELayer, dev)
+        return
+    if args.prefill:
+        prefill_run(args, torch, synth, PagedMoELayer, dev)
         return
     cfg = synth.CONFIGS["qwen_d2048_t16"]
     T = cfg.T
@@ -698,6 +770,9 @@ def main():
         log(f"page movement: forward p50 {pg['forward_us_quiet']['p50']} -> {pg['forward_us_while_moving']['p50']} us, "
             f"p99 {pg['forward_us_quiet']['p99']} -> {pg['forward_us_while_moving']['p99']} us, "
             f"{pg['copied_MB']} MB at {pg['copy_GBps']} GB/s; planner {pg['planner']['host_us']} us")
+        subs["prefill_t1024"] = prefill_run(args, torch, synth, PagedMoELayer, dev, print_table=False)
+        log(f"prefill T=1024: {subs['prefill_t1024']['value']:,.0f} tokens/s, "
+            f"{subs['prefill_t1024']['useful_mfma_TFLOPs']} useful MFMA TFLOP/s")
         subs["kv_pressure"] = kv_pressure_run(args, torch, synth, PagedMoELayer, dev, print_table=False)
         kp = subs["kv_pressure"]
         log(f"kv pressure: {kp['plan_changes']} plan changes, weights {kp['weights_MB']} MB, "

@@ -96,6 +96,11 @@ typedef struct {
                               max_tokens*(top_k+1)*max(d_ffn, d_ffn_shared) < 2^31 */
     uint32_t flags;        /* 0, or PW_FLAG_LUT_TILED: every bound LUT page of this layer
                               is in the 32-row tiled order (default: row-major) */
+    int32_t rows_per_block;/* linear-block size: 0 = one block per linear; else a multiple
+                              of 64 dividing d_model, d_ffn and d_ffn_shared, and every
+                              linear is cut into row-blocks of that many rows, each a
+                              block with its own bitwidth and pages (legiblepapers "Key
+                              Takeaways" and FAQ Q5: bitwidths vary per linear-block) */
 } pw_moe_desc;
 
 #define PW_FLAG_LUT_TILED 1u
@@ -124,23 +129,43 @@ pw_status pw_layer_destroy(pw_layer layer);
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 const char* pw_last_error(void);
 
-/* Sets the bitwidth plan: bits[e*3 + l] for e in [0, E + has_shared), l in
- * {PW_GATE, PW_UP, PW_DOWN}, each in 1..8 (host array, copied before return).
- * n_blocks must equal 3*(E + has_shared). The plan takes effect at the next
+/* Blocks. With rows_per_block = 0 block e*3 + l is linear l in {PW_GATE, PW_UP,
+ * PW_DOWN} of expert e in [0, E + has_shared). With rows_per_block = rb > 0 the
+ * blocks are numbered expert by expert (routed 0..E-1, then the shared
+ * expert), within an expert gate, up, down, and within a linear by row-block j
+ * (rows j*rb .. j*rb + rb - 1): expert e (ffn f) owns 2*f/rb + d_model/rb
+ * blocks. The planner's arrays (sensitivity, residual, min/max, bits) use the
+ * same order.
+ *
+ * Sets the bitwidth plan: bits[i] for every block i, each in 1..8 (host array,
+ * copied before return); n_blocks must equal the layer's block count. The plan takes effect at the next
  * forward, which uploads the tables in stream order before its kernels, so a
  * rewrite between two forwards needs no host synchronisation. */
 pw_status pw_moe_plan_set(pw_layer layer, const uint8_t* bits, int32_t n_blocks);
 
-/* Binds the pages of block (expert, linear): planes[p] for p < n_planes are
+/* Binds the pages of linear (expert, linear): planes[p] for p < n_planes are
  * device pointers to bit-plane p (planes 0..n_planes-1 of the parent, 16-byte
- * aligned, R*K/8 bytes each); lut is a device pointer to LUT_{lut_bits}
- * (R * 2^lut_bits fp16 in the layer's LUT page order above, 16-byte aligned). The host
- * array `planes` is copied before return. The pages must stay alive until every forward enqueued while
+ * aligned, R*K/8 bytes each, the whole linear); lut is a device pointer to
+ * LUT_{lut_bits} (R * 2^lut_bits fp16 in the layer's LUT page order above,
+ * 16-byte aligned). With row-blocks, every row-block of the linear is bound to
+ * its rows of these pages at lut_bits. The host array `planes` is copied
+ * before return. The pages must stay alive until every forward enqueued while
  * they were bound has completed on its stream. A forward requires, for every
  * block, n_planes >= b and lut_bits == b for the planned b (else PW_E_UNBOUND). */
 pw_status pw_page_table_bind(pw_layer layer, int32_t expert, int32_t linear,
                              const void* const* planes, int32_t n_planes,
                              const void* lut, int32_t lut_bits);
+
+/* Binds the pages of one block: row-block row_block of linear (expert, linear)
+ * (0 when the layer's linears are whole). planes[p] are device pointers to the
+ * block's rows of bit-plane p (rows x K/8 bytes, 16-byte aligned), lut to the
+ * block's rows of LUT_{lut_bits} (rows * 2^lut_bits fp16, layer's page order;
+ * in the tiled order the block's rows form whole 32-row tiles). Same
+ * lifetime rules as pw_page_table_bind; PW_E_ARG for a row_block outside the
+ * linear. */
+pw_status pw_page_table_bind_rows(pw_layer layer, int32_t expert, int32_t linear, int32_t row_block,
+                                  const void* const* planes, int32_t n_planes,
+                                  const void* lut, int32_t lut_bits);
 
 /* One MoE layer on T tokens, enqueued on `stream` (hipStream_t as void*; NULL =
  * the null stream); asynchronous, no host synchronisation.
@@ -195,7 +220,7 @@ pw_status pw_moe_forward_noalloc(pw_layer layer, const void* x, int32_t T, const
 
 /* Quality-aware runtime planner (legiblepapers "Summary & Methodology Analysis"
  * and FAQ Q8): from the layer's current plan, greedily choose one-bit
- * bitwidth changes per block (expert, linear) until bytes_to_free bytes of
+ * bitwidth changes per block until bytes_to_free bytes of
  * pages are released, taking at each step the action with the least damage per
  * released byte. bytes_to_free < 0 is a budget to spend instead: upgrades with
  * the most benefit per added byte are taken while they fit. Host-only (no GPU
@@ -207,6 +232,7 @@ pw_status pw_moe_forward_noalloc(pw_layer layer, const void* x, int32_t T, const
  *   (quantisation noise power of a b-bit quantiser scales as 4^-b), with
  *   mass_e = expert_count[e] / n_tokens for a routed expert (how often it is
  *   used) and 1 for the shared expert. Ties go to the lower block index.
+ *   A block is a (row-block of a) linear, numbered as for pw_moe_plan_set.
  *   sensitivity  host float [n_blocks], finite, >= 0 (offline sensitivity)
  *   residual     host float [n_blocks], finite, >= 0, or NULL (prompt residuals)
  *   expert_count host int32 [n_experts] >= 0 (e.g. pw_route_out.expert_count of

@@ -60,7 +60,7 @@ def lib():
         L.orc_dequant.restype = None
         L.orc_linear.argtypes = [P, i32, P, i32, i32, P, P]
         L.orc_linear.restype = None
-        L.orc_moe_forward.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, i32, P,
+        L.orc_moe_forward.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, i32, P,
                                       P, P, P, P, P, P, i32]
         L.orc_moe_forward.restype = i32
         L.orc_residual.argtypes = [P, P, ctypes.c_size_t, P]
@@ -167,40 +167,61 @@ def residual(x, y):
 class OracleLayer:
     """The oracle's own copy of one layer: bitwidth plan plus the generator's
     planes and LUTs per (expert, linear). A plan change is a new `bits` array;
-    the layer keeps no other state (O8)."""
+    the layer keeps no other state (O8).
 
-    def __init__(self, d, E, F, k, Fs, bits, blocks):
+    rows_per_block = 0: one linear-block per linear, bits [E + has_shared, 3].
+    rows_per_block = rb > 0: each linear is split into blocks of rb rows, bits is
+    flat, one entry per block in the order expert (routed, then shared), linear
+    (gate, up, down), row-block; block j of a linear reads rows j*rb .. j*rb+rb-1
+    of that linear's planes and of its LUT at the block's own bitwidth."""
+
+    def __init__(self, d, E, F, k, Fs, bits, blocks, rows_per_block=0):
         self.d, self.E, self.F, self.k, self.Fs = int(d), int(E), int(F), int(k), int(Fs)
+        self.rb = int(rows_per_block)
         self.n_total = self.E + (1 if self.Fs > 0 else 0)
         self.blocks = blocks            # (e, lin) -> object with .planes and .luts
         self.set_bits(bits)
 
     @classmethod
-    def from_config(cls, cfg, bits, blocks):
-        return cls(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, bits, blocks)
+    def from_config(cls, cfg, bits, blocks, rows_per_block=0):
+        return cls(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, bits, blocks, rows_per_block)
+
+    def block_list(self):
+        """(e, lin, first row, rows) of every block in order."""
+        out = []
+        for e in range(self.n_total):
+            f = self.Fs if e == self.E else self.F
+            for lin in range(3):
+                R = self.d if lin == 2 else f
+                rows = self.rb or R
+                for j in range(R // rows):
+                    out.append((e, lin, j * rows, rows))
+        return out
 
     def set_bits(self, bits):
-        bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8).reshape(self.n_total, 3))
+        blist = self.block_list()
+        bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8).reshape(-1))
+        if bits.shape[0] != len(blist):
+            raise ValueError(f"{bits.shape[0]} bitwidths for {len(blist)} blocks")
         self._bits = bits
-        self._plane_arr = (ctypes.c_void_p * (self.n_total * 3 * 8))()
-        self._lut_arr = (ctypes.c_void_p * (self.n_total * 3))()
+        self._plane_arr = (ctypes.c_void_p * (len(blist) * 8))()
+        self._lut_arr = (ctypes.c_void_p * len(blist))()
         self._keep = []
-        for e in range(self.n_total):
-            for lin in range(3):
-                b = int(bits[e, lin])
-                blk = self.blocks[(e, lin)]
-                planes = np.ascontiguousarray(blk.planes, dtype=np.uint8)
-                if planes.shape[0] < b:
-                    raise ValueError(f"block {(e, lin)} has {planes.shape[0]} planes < b={b}")
-                lut_b = _h(blk.luts[b])
-                self._keep += [planes, lut_b]
-                for p in range(b):
-                    self._plane_arr[(e * 3 + lin) * 8 + p] = planes[p].ctypes.data
-                self._lut_arr[e * 3 + lin] = lut_b.ctypes.data
+        for i, (e, lin, r0, rows) in enumerate(blist):
+            b = int(bits[i])
+            blk = self.blocks[(e, lin)]
+            planes = np.ascontiguousarray(blk.planes, dtype=np.uint8)
+            if planes.shape[0] < b:
+                raise ValueError(f"block {(e, lin)} has {planes.shape[0]} planes < b={b}")
+            lut_b = _h(blk.luts[b])
+            self._keep += [planes, lut_b]
+            for p in range(b):
+                self._plane_arr[i * 8 + p] = planes[p, r0:r0 + rows].ctypes.data
+            self._lut_arr[i] = lut_b[r0:r0 + rows].ctypes.data
 
     @property
     def bits(self):
-        return self._bits.copy()
+        return self._bits.reshape(self.n_total, 3).copy() if not self.rb else self._bits.copy()
 
     def forward(self, x, router_w, router_b=None, subset=None, threads: int = 0):
         """Returns dict(y, logits, ids, w, counts, offsets, sorted, status).
@@ -219,7 +240,7 @@ class OracleLayer:
         offsets = np.zeros(self.E + 1, dtype=np.int32)
         srt = np.zeros(T * self.k, dtype=np.int32)
         st = lib().orc_moe_forward(
-            self.d, self.E, self.F, self.Fs, self.k, _p(self._bits), self._plane_arr, self._lut_arr,
+            self.d, self.E, self.F, self.Fs, self.k, self.rb, _p(self._bits), self._plane_arr, self._lut_arr,
             _p(xh), T, _p(wh), _p(bh), _p(sub), 0 if sub is None else len(sub), _p(y), _p(L),
             _p(ids), _p(w), _p(counts), _p(offsets), _p(srt), int(threads))
         return dict(y=y, logits=L, ids=ids, w=w, counts=counts, offsets=offsets, sorted=srt,

@@ -199,12 +199,39 @@ void orc_linear(const uint8_t* const* planes, int b, const uint16_t* lut, int R,
 
 /* ---------------------------------------------------------------- O6 expert */
 
+/* Linear-blocks. A linear-block is a whole linear (rb = 0), or, with rb > 0, a
+ * block of rb consecutive rows of a linear (legiblepapers "Key Takeaways" and
+ * FAQ Q5: variable bitwidths per linear-block; the pages do not say how large a
+ * block is, so both readings are served). Blocks are numbered expert by expert
+ * (routed 0..E-1, then the shared expert), within an expert gate, up, down, and
+ * within a linear by row-block. Each block has its own bitwidth, planes (its
+ * rows only, row-major) and LUT (its rows only). */
 typedef struct {
     int d, E, F, Fs, k;
-    const uint8_t* bits;            /* [n_total * 3] */
-    const uint8_t* const* planes;   /* [n_total * 3 * 8], NULL beyond b */
-    const uint16_t* const* luts;    /* [n_total * 3], LUT for that block's b */
+    int rb;                         /* rows per linear-block; 0 = whole linears */
+    const uint8_t* bits;            /* [n_blocks] */
+    const uint8_t* const* planes;   /* [n_blocks * 8], NULL beyond b */
+    const uint16_t* const* luts;    /* [n_blocks], LUT for that block's b */
 } orc_layer;
+
+/* row-blocks of a linear with R rows */
+static int n_rowblocks(const orc_layer* L, int R) { return L->rb ? R / L->rb : 1; }
+
+/* index of the first block of expert e (the shared expert, e = E, follows the routed ones) */
+static size_t expert_base(const orc_layer* L, int e) {
+    return (size_t)e * (size_t)(2 * n_rowblocks(L, L->F) + n_rowblocks(L, L->d));
+}
+
+/* out[r] = sum_c W[r][c] * v[c] for a linear of R rows whose row-blocks are blocks
+ * base, base+1, ...: row r is row r - j*rows of block base + j, j = r / rows,
+ * read at that block's bitwidth (rows = rb, or R for a whole linear). */
+static void linear_blocks_f32(const orc_layer* L, size_t base, int R, int K, const float* v, float* out) {
+    int rows = L->rb ? L->rb : R;
+    for (int j = 0; j * rows < R; ++j) {
+        size_t bi = base + (size_t)j;
+        linear_f32(L->planes + bi * 8, L->bits[bi], L->luts[bi], rows, K, v, out + (size_t)j * rows);
+    }
+}
 
 static float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -212,16 +239,14 @@ static float silu(float z) { return z / (1.0f + expf(-z)); }
 static void expert_forward(const orc_layer* L, int e, const float* xv, float* o) {
     int f = (e == L->E) ? L->Fs : L->F;
     int d = L->d;
-    const uint8_t* const* pg = L->planes + ((size_t)e * 3 + 0) * 8;
-    const uint8_t* const* pu = L->planes + ((size_t)e * 3 + 1) * 8;
-    const uint8_t* const* pd = L->planes + ((size_t)e * 3 + 2) * 8;
-    int bg = L->bits[e * 3 + 0], bu = L->bits[e * 3 + 1], bd = L->bits[e * 3 + 2];
+    size_t base = expert_base(L, e);
+    int nf = n_rowblocks(L, f);
     float* g = (float*)malloc(sizeof(float) * (size_t)f);
     float* u = (float*)malloc(sizeof(float) * (size_t)f);
-    linear_f32(pg, bg, L->luts[e * 3 + 0], f, d, xv, g);
-    linear_f32(pu, bu, L->luts[e * 3 + 1], f, d, xv, u);
+    linear_blocks_f32(L, base, f, d, xv, g);              /* gate */
+    linear_blocks_f32(L, base + nf, f, d, xv, u);         /* up */
     for (int r = 0; r < f; ++r) g[r] = silu(g[r]) * u[r];
-    linear_f32(pd, bd, L->luts[e * 3 + 2], d, f, g, o);
+    linear_blocks_f32(L, base + 2 * nf, d, f, g, o);      /* down */
     free(g);
     free(u);
 }
@@ -229,23 +254,26 @@ static void expert_forward(const orc_layer* L, int e, const float* xv, float* o)
 /* ---------------------------------------------------------------- whole layer */
 
 /*
- * Full layer on T tokens. Routing (logits, ids, w, counts, offsets, sorted) is
+ * Full layer on T tokens, linear-blocks of rb rows (0: whole linears; bits,
+ * planes and luts then hold one entry per block in the order above). Routing
+ * (logits, ids, w, counts, offsets, sorted) is
  * computed for all tokens; the expert outputs y[t][:] only for the tokens listed
  * in `subset` (all tokens when subset == NULL). y is [T][d], fp32; rows outside
  * the subset are left untouched. Any routing output pointer may be NULL.
  * Returns ORC_OK or ORC_E_RANGE (logit out of int64 range / non-finite input).
  */
-int orc_moe_forward(int d, int E, int F, int Fs, int k, const uint8_t* bits,
+int orc_moe_forward(int d, int E, int F, int Fs, int k, int rb, const uint8_t* bits,
                     const uint8_t* const* planes, const uint16_t* const* luts,
                     const uint16_t* x, int T, const uint16_t* router_w, const uint16_t* router_b,
                     const int32_t* subset, int n_subset, float* y, int64_t* logits_out,
                     int32_t* ids_out, float* w_out, int32_t* counts_out, int32_t* offsets_out,
                     int32_t* sorted_out, int nthreads) {
-    if (T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E || k > 64) return ORC_E_ARG;
+    if (T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E || k > 64 || rb < 0) return ORC_E_ARG;
+    if (rb && (d % rb || F % rb || (Fs > 0 && Fs % rb))) return ORC_E_ARG;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #endif
-    orc_layer Ly = {d, E, F, Fs, k, bits, planes, luts};
+    orc_layer Ly = {d, E, F, Fs, k, rb, bits, planes, luts};
     int64_t* Lg = (int64_t*)malloc(sizeof(int64_t) * ((size_t)T * E + 1));
     int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * k + 1));
     float* w = (float*)malloc(sizeof(float) * ((size_t)T * k + 1));

@@ -43,22 +43,26 @@ def noise(b: int) -> float:
     return 2.0 ** (-2 * b)
 
 
-def block_shapes(d: int, E: int, F: int, Fs: int):
-    """(R, K) of every block in (expert, linear) order: gate and up [F x d], down [d x F];
-    the shared expert (id E, when Fs > 0) uses Fs."""
+def block_shapes(d: int, E: int, F: int, Fs: int, rows_per_block: int = 0):
+    """(R, K) of every block in (expert, linear, row-block) order: gate and up [F x d], down
+    [d x F], the shared expert (id E, when Fs > 0) with Fs; with rows_per_block = rb > 0 each
+    linear is cut into blocks of rb rows."""
     shapes = []
     for e in range(E + (1 if Fs > 0 else 0)):
         f = Fs if e == E else F
-        shapes += [(f, d), (f, d), (d, f)]
+        for R, K in ((f, d), (f, d), (d, f)):
+            rows = rows_per_block or R
+            shapes += [(rows, K)] * (R // rows)
     return shapes
 
 
-def masses(E: int, has_shared: bool, expert_count, T: int):
-    """Routing mass per block: count_e / T for routed experts, 1 for the shared expert."""
+def masses(E: int, has_shared: bool, expert_count, T: int, blocks_per_expert=None):
+    """Routing mass per block: count_e / T for routed experts, 1 for the shared expert;
+    blocks_per_expert[e] blocks per expert (3 when linears are whole)."""
     m = []
     for e in range(E + (1 if has_shared else 0)):
         me = 1.0 if e == E else float(expert_count[e]) / float(T)
-        m += [me, me, me]
+        m += [me] * (3 if blocks_per_expert is None else blocks_per_expert[e])
     return m
 
 

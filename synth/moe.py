@@ -98,7 +98,13 @@ CONFIGS = {
                     bits_rule="uniform", bits_values=(3, 4, 5, 6, 8),
                     layers=24, steps=64, rewrite_every=16, rewrite_frac=0.25,
                     rewrite_drop=2),
+    # the decode layer's shape at prefill scale, with linear-blocks of 128 rows
+    "qwen_rows128_t1024": MoEConfig("qwen_rows128_t1024", 5, d=2048, E=60, F=1408, k=4, T=1024, Fs=5632,
+                    bits_rule="uniform", bits_values=(3, 4, 5, 6, 8)),
 }
+
+# rows per linear-block of the workloads cut into row-blocks (the rest: whole linears)
+ROWS_PER_BLOCK = {"qwen_rows128_t1024": 128}
 
 WORKLOAD_TEXT = {
     "tiny_d256": "d256 E8 F512 top2 T4, bits U{3,4}",
@@ -106,6 +112,7 @@ WORKLOAD_TEXT = {
     "mixtral_d4096": "Mixtral-8x7B-shaped layer: d4096 E8 F14336 top2, bits {3,4,6,8} p=(.3,.3,.2,.2), Zipf(1.2) routing",
     "fine_e128_t128": "fine-grained layer: d2048 E128 F768 top8 T128, Zipf(1.1) routing, bits by routed frequency 8/4/3",
     "qwen_stack24_t256": "24-layer stack of the d2048 E60 F1408 top4 (+shared F5632) layer, T256, 64 steps, plan rewrite every 16",
+    "qwen_rows128_t1024": "prefill of the d2048 E60 F1408 top4 (+shared F5632) layer, T1024, linear-blocks of 128 rows, bits U{3,4,5,6,8} per block",
 }
 
 
@@ -193,6 +200,27 @@ def initial_bits(cfg: MoEConfig, *, layer: int = 0, run_seed: int = 0,
     if cfg.bits_rule == "choice":
         return g.choice(vals, size=(n, 3), p=np.asarray(cfg.bits_probs)).astype(np.uint8)
     raise ValueError(cfg.bits_rule)
+
+
+def n_row_blocks(cfg: MoEConfig, rows_per_block: int) -> int:
+    """Blocks of a layer when every linear is split into blocks of rows_per_block rows
+    (0: whole linears): per expert 2 * ffn / rb + d / rb."""
+    if rows_per_block <= 0:
+        return cfg.n_blocks
+    n = 0
+    for e in range(cfg.n_experts_total):
+        n += 2 * cfg.ffn(e) // rows_per_block + cfg.d // rows_per_block
+    return n
+
+
+def rowblock_bits(cfg: MoEConfig, rows_per_block: int, *, layer: int = 0, run_seed: int = 0) -> np.ndarray:
+    """Flat per-block bitwidths for row-blocks of rows_per_block rows (order: expert, linear,
+    row-block), drawn per block like the config's uniform / choice rule."""
+    n = n_row_blocks(cfg, rows_per_block)
+    g = rng_for(cfg, run_seed, layer=layer, kind=KIND_BITS, b=rows_per_block)
+    vals = np.asarray(cfg.bits_values, dtype=np.uint8)
+    p = None if cfg.bits_rule == "uniform" else np.asarray(cfg.bits_probs)
+    return g.choice(vals, size=n, p=p).astype(np.uint8)
 
 
 def plan_by_frequency(counts: np.ndarray, n_experts_total: int, tiers=(8, 4, 3),

@@ -201,3 +201,29 @@ def test_noalloc_validation(B):
         B.pw_moe_forward_noalloc(h, 4096, 0, 4096, 0, 4096)   # T = 0: a no-op
     finally:
         B.pw_layer_destroy(h)
+
+
+def test_row_block_validation(B):
+    ok = dict(d_model=256, n_experts=4, d_ffn=384, top_k=2, d_ffn_shared=512, max_tokens=8)
+    for rb in (32, 96, 100, -64, 256):   # not a multiple of 64, not dividing every size, negative
+        with pytest.raises(B.PwError) as ei:
+            B.pw_layer_create(**ok, rows_per_block=rb)
+        assert ei.value.status == 2, rb
+    h = B.pw_layer_create(**ok, rows_per_block=128)
+    try:
+        # blocks: per routed expert 2*384/128 + 256/128 = 8, the shared 2*512/128 + 2 = 10
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_plan_set(h, [3] * 3 * 5)
+        assert ei.value.status == 1
+        B.pw_moe_plan_set(h, [3] * (4 * 8 + 10))
+        base = 1 << 40
+        planes = [base + 4096 * p for p in range(3)]
+        with pytest.raises(B.PwError) as ei:
+            B.pw_page_table_bind_rows(h, 0, 0, 3, planes, base + (1 << 20), 3)   # gate has 3 row-blocks
+        assert ei.value.status == 1
+        B.pw_page_table_bind_rows(h, 4, 2, 1, planes, base + (1 << 20), 3)       # shared down, row-block 1
+        with pytest.raises(B.PwError) as ei:
+            B.pw_moe_forward(h, 4096, 1, 4096, 0, 4096)
+        assert ei.value.status == 4                                                # others unbound
+    finally:
+        B.pw_layer_destroy(h)

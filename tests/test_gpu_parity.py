@@ -79,7 +79,8 @@ def run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=None, pa
     y = lay.forward(xd, wd, bd, route=route)
     torch.cuda.synchronize()
     assert lay.status() == 0
-    ref = oracle.OracleLayer.from_config(cfg, bits, blocks).forward(x, wr, bias, subset=subset)
+    ref = oracle.OracleLayer.from_config(cfg, bits, blocks, rows_per_block=lay.rows_per_block).forward(
+        x, wr, bias, subset=subset)
     check_routing(route, ref, T, cfg.E, cfg.k)
     yh = y.cpu().numpy()
     err = rel_err_per_token(yh[subset], ref["y"][subset])
@@ -603,3 +604,52 @@ def test_kv_pressure_plans(torch_dev):
         run_parity(torch_dev, cfg, pm.bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
                    pages=pm.dev)
     assert seen == {"down", "up"}
+
+
+def _row_block_layer(torch_dev, cfg, rb, bits, lut_tiled=False, max_tokens=None):
+    """A layer of rb-row linear-blocks bound block by block to its rows of whole-linear pages."""
+    torch, dev = torch_dev
+    from any_precision_bit_amd import PagedMoELayer
+
+    jobs = [(e, lin) for e in range(cfg.n_experts_total) for lin in synth.LINEARS]
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=(3, 4, 5, 6, 8)) for e, lin in jobs}
+    pages = device_pages(blocks, np.full((cfg.n_experts_total, 3), 8), dev, all_luts=True, lut_tiled=lut_tiled)
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, max_tokens or cfg.T, lut_tiled=lut_tiled,
+                        rows_per_block=rb)
+    lay.plan_set(bits)
+    i = 0
+    for e, lin in jobs:
+        planes, luts = pages[(e, lin)]
+        R = planes.shape[1]
+        for j in range(R // rb):
+            b = int(bits[i])
+            i += 1
+            rows = slice(j * rb, (j + 1) * rb)
+            lay.bind_rows(e, lin, j, [planes[p][rows] for p in range(b)], luts[b][rows], b)
+    assert i == bits.shape[0]
+    return lay, blocks, pages
+
+
+@pytest.mark.parametrize("lut_tiled", [False, True])
+def test_row_blocks_decode(torch_dev, lut_tiled):
+    """qwen_d2048_t16 with linear-blocks of 128 rows, each at its own bitwidth (per-block pages bound
+    one by one), against the oracle on every token."""
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    bits = synth.rowblock_bits(cfg, 128)
+    _say(f"row-blocks of 128 rows, lut_tiled={lut_tiled}: {bits.shape[0]} blocks")
+    lay, blocks, pages = _row_block_layer(torch_dev, cfg, 128, bits, lut_tiled)
+    x, wr, bias = layer_inputs(cfg)
+    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32), layer=lay,
+               pages=pages)
+
+
+def test_prefill_t1024_row_blocks(torch_dev):
+    """The T = 1024 prefill workload (qwen_rows128_t1024): routing on all 1024 tokens, outputs on 48
+    seeded tokens, linear-blocks of 128 rows."""
+    cfg = synth.CONFIGS["qwen_rows128_t1024"]
+    rb = synth.ROWS_PER_BLOCK[cfg.name]
+    bits = synth.rowblock_bits(cfg, rb)
+    lay, blocks, pages = _row_block_layer(torch_dev, cfg, rb, bits)
+    x, wr, bias = layer_inputs(cfg)
+    _say("qwen_rows128_t1024")
+    run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, sample_tokens(cfg.T, 48, seed=9), layer=lay, pages=pages)

@@ -391,3 +391,61 @@ def test_frequency_plan():
     assert bits[1].tolist() == [8, 8, 8] and bits[2].tolist() == [8, 8, 8]
     assert bits[4].tolist() == [4, 4, 4] and bits[0].tolist() == [4, 4, 4]
     assert bits[3].tolist() == [3, 3, 3]
+
+
+# ----------------------------------------------------------------------------- linear-blocks of row-blocks
+def test_rowblocks_with_one_bitwidth_per_linear_equal_whole_linears():
+    """Row-blocks that all carry their linear's bitwidth reproduce the whole-linear layer bitwise."""
+    cfg = SMALL
+    bits = synth.initial_bits(cfg)
+    blocks = synth.make_layer_blocks(cfg, bits)
+    x = synth.tokens(cfg)
+    wr, bias = synth.router(cfg)
+    whole = oracle.OracleLayer.from_config(cfg, bits, blocks).forward(x, wr, bias)
+    rb = 64
+    flat = []
+    for e in range(cfg.n_experts_total):
+        for lin in range(3):
+            R = cfg.d if lin == DOWN else cfg.ffn(e)
+            flat += [bits[e, lin]] * (R // rb)
+    rows = oracle.OracleLayer.from_config(cfg, np.array(flat, np.uint8), blocks, rows_per_block=rb).forward(x, wr, bias)
+    assert np.array_equal(whole["y"].view(np.uint32), rows["y"].view(np.uint32))
+
+
+@pytest.mark.parametrize("rb", [64, 128])
+def test_rowblocks_vs_dense_fp64(rb):
+    """Per-row-block bitwidths against a dense fp64 layer whose weights are materialised row by row
+    from the parent indices at the row's block bitwidth."""
+    cfg = SMALL
+    flat = synth.rowblock_bits(cfg, rb)
+    assert len(set(flat.tolist())) > 2
+    blocks = {(e, lin): synth.make_block(cfg, e, lin, n_planes=8, lut_bits=(3, 4, 5, 6, 8), keep_parent=True)
+              for e in range(cfg.n_experts_total) for lin in range(3)}
+    x = synth.tokens(cfg)
+    wr, bias = synth.router(cfg)
+    out = oracle.OracleLayer.from_config(cfg, flat, blocks, rows_per_block=rb).forward(x, wr, bias)
+    # materialise every linear row by row at its block's bitwidth
+    W, i = {}, 0
+    for e in range(cfg.n_experts_total):
+        for lin in range(3):
+            blk = blocks[(e, lin)]
+            Wm = np.zeros((blk.R, blk.K))
+            for j in range(blk.R // rb):
+                b = int(flat[i])
+                i += 1
+                rr = np.arange(j * rb, (j + 1) * rb)
+                Wm[rr] = blk.luts[b][rr[:, None], blk.q[rr] >> (8 - b)]
+            W[(e, lin)] = Wm
+    L = exact_logits_py(x, wr, bias)
+    y = np.zeros((cfg.T, cfg.d))
+    xf = x.astype(np.float64)
+    expert = lambda e, v: W[(e, DOWN)] @ ((lambda g, u: g / (1.0 + np.exp(-g)) * u)(W[(e, GATE)] @ v, W[(e, UP)] @ v))
+    for t in range(cfg.T):
+        order = sorted(range(cfg.E), key=lambda e: (-L[t][e], e))[:cfg.k]
+        lg = np.array([L[t][e] for e in order], dtype=np.float64) * 2.0 ** -48
+        ww = np.exp(lg - lg[0])
+        ww /= ww.sum()
+        for j, e in enumerate(order):
+            y[t] += ww[j] * expert(e, xf[t])
+        y[t] += expert(cfg.E, xf[t])
+    assert rel_err_per_token(out["y"].astype(np.float64), y).max() <= 1e-5

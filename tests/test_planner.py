@@ -181,3 +181,28 @@ def test_library_planner_validation(B):
         assert out.tolist() == [3, 4, 5] * 4 and n >= 0
     finally:
         B.pw_layer_destroy(h)
+
+
+def test_library_planner_row_blocks_matches_oracle(B):
+    """Linear-blocks of 128 rows: the planner works on every row-block."""
+    g = np.random.default_rng(7)
+    cfg = synth.CONFIGS["qwen_d2048_t16"]
+    rb = 128
+    h = B.pw_layer_create(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, cfg.T, rows_per_block=rb)
+    try:
+        bits = synth.rowblock_bits(cfg, rb)
+        n = bits.shape[0]
+        B.pw_moe_plan_set(h, bits)
+        shapes = P.block_shapes(cfg.d, cfg.E, cfg.F, cfg.Fs, rb)
+        assert len(shapes) == n == synth.n_row_blocks(cfg, rb)
+        per = [2 * cfg.ffn(e) // rb + cfg.d // rb for e in range(cfg.n_experts_total)]
+        sens = g.random(n).astype(np.float32)
+        counts = g.multinomial(cfg.T * cfg.k, np.ones(cfg.E) / cfg.E).astype(np.int32)
+        mass = P.masses(cfg.E, True, counts, cfg.T, per)
+        total = sum(P.block_bytes(R, K, int(b)) for (R, K), b in zip(shapes, bits))
+        for frac in (0.1, -0.2):
+            got = B.pw_plan_greedy(h, sens, counts, cfg.T, frac * total)
+            ref = P.plan(shapes, bits, sens, mass, frac * total)
+            assert np.array_equal(got[0], ref[0]) and got[1] == ref[1] and got[3] == ref[3]
+    finally:
+        B.pw_layer_destroy(h)
