@@ -367,7 +367,8 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     gp.ld_act = f_max;
     gp.shared_base = shared_base;
     gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
-    gp.rb = D.rows_per_block;
+    gp.rb_lg = 0;
+    while (D.rows_per_block > 0 && (1 << gp.rb_lg) < D.rows_per_block) ++gp.rb_lg;
     gp.y = y;
     // gate_up + SwiGLU: items of 32 rows of F (gate and up)
     r.gu = gp;
@@ -471,11 +472,11 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     if (D.abi_version != PW_ABI_VERSION)
         return fail(PW_E_ARG, "abi_version %d, library is %d", D.abi_version, PW_ABI_VERSION);
     if (D.flags & ~PW_FLAG_LUT_TILED) return fail(PW_E_ARG, "flags 0x%x: only PW_FLAG_LUT_TILED is defined", D.flags);
-    if (D.rows_per_block < 0 || D.rows_per_block % 64 ||
+    if (D.rows_per_block < 0 || D.rows_per_block % 64 || (D.rows_per_block & (D.rows_per_block - 1)) ||
         (D.rows_per_block > 0 && (D.d_model % D.rows_per_block || D.d_ffn % D.rows_per_block ||
                                   D.d_ffn_shared % D.rows_per_block)))
-        return fail(PW_E_SHAPE, "rows_per_block %d: must be 0 or a multiple of 64 dividing d_model, d_ffn and "
-                    "d_ffn_shared", D.rows_per_block);
+        return fail(PW_E_SHAPE, "rows_per_block %d: must be 0 or a power of two of at least 64 dividing d_model, "
+                    "d_ffn and d_ffn_shared", D.rows_per_block);
     if (D.d_model <= 0 || D.d_model % 128 || D.d_model > pw::kMaxModel)
         return fail(PW_E_SHAPE, "d_model %d: must be a positive multiple of 128, at most %d", D.d_model,
                     pw::kMaxModel);

@@ -84,8 +84,8 @@ struct GemmParams {
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
     int lut_tiled;            // LUT pages in the 32-row tiled order (else row-major)
-    int rb;                   // rows per linear-block (0: whole linears); blocks are numbered
-                              // expert, linear, row-block
+    int rb_lg;                // log2 of the rows per linear-block (0: whole linears); blocks
+                              // are numbered expert, linear, row-block
     const uint16_t* x;        // layer input (gate_up B operand)
     uint32_t b_bytes;         // size of the B-operand buffer (x or act)
     float* y;

@@ -605,8 +605,8 @@ struct Item {
     int n_tok, tbase, nl;     // tokens of the expert, first token of the group, tokens here
     int K, R;                 // columns / rows of the block
     int kbase, klen;          // K range of this item
-    int rows0, rows1;         // first row of set 0 / set 1 within its block's pages
-    int abs0, abs1;           // the same rows within the whole linear (output rows / act columns)
+    int rows0, rows1;         // first row of set 0 / set 1 within its block's pages (within
+                              // the linear: tile * 32 for gate_up, tile * 64 (+ 32) for down)
     const __attribute__((address_space(4))) DevBlock* blk0;   // page-table entries (scalar loads)
     const __attribute__((address_space(4))) DevBlock* blk1;
 };
@@ -662,29 +662,28 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p, const int* s_pr
     it.tbase = it.grp * 16 * NT;
     it.nl = min(16 * NT, it.n_tok - it.tbase);
     // Blocks are numbered expert by expert, then gate, up, down, then row-block:
-    // with p.rb rows per block (0: whole linears) expert ex owns 2*f/rb + d/rb
-    // blocks (the shared expert, ex = E, follows the routed ones), and the item's
-    // rows lie in row-block j of its linear, whose pages start at row j*rb.
+    // with 2^rb_lg rows per block (rb_lg = 0: whole linears) expert ex owns
+    // 2*f/rb + d/rb blocks (the shared expert, ex = E, follows the routed ones),
+    // and the item's rows lie in row-block j of its linear, whose pages start at
+    // row j*rb.
     const int f = sh ? p.Fs : p.F;
-    const int nF = p.rb ? f / p.rb : 1;
-    const int base = it.ex * (p.rb ? 2 * (p.F / p.rb) + p.d / p.rb : 3);
+    const int lg = p.rb_lg;
+    const int nF = lg ? f >> lg : 1;
+    const int base = it.ex * (lg ? 2 * (p.F >> lg) + (p.d >> lg) : 3);
     const int arow = it.tile * (MODE == 0 ? 32 : 64);
-    const int j = p.rb ? arow / p.rb : 0;
-    const int roff = j * p.rb;
-    it.abs0 = arow;
+    const int j = lg ? arow >> lg : 0;
+    const int rel = arow - (j << lg);
     if (MODE == 0) {
         it.K = p.d;
-        it.R = p.rb ? p.rb : f;
-        it.abs1 = arow;
-        it.rows0 = it.rows1 = arow - roff;
+        it.R = lg ? 1 << lg : f;
+        it.rows0 = it.rows1 = rel;
         it.blk0 = kconst(p.blocks) + base + j;
         it.blk1 = kconst(p.blocks) + base + nF + j;
     } else {
         it.K = f;
-        it.R = p.rb ? p.rb : p.d;
-        it.abs1 = arow + 32;
-        it.rows0 = arow - roff;
-        it.rows1 = arow - roff + 32;
+        it.R = lg ? 1 << lg : p.d;
+        it.rows0 = rel;
+        it.rows1 = rel + 32;
         it.blk0 = it.blk1 = kconst(p.blocks) + base + 2 * nF + j;
     }
     it.kbase = piece * kDownPiece;
@@ -1067,7 +1066,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     if (it.mode == 0) {
                         const float a0 = g0 / (1.0f + expf(-g0)) * u0;
                         const float a1 = g1 / (1.0f + expf(-g1)) * u1;
-                        const int f = it.abs0 + row;   // even: f, f+1 are adjacent act columns
+                        const int f = it.tile * 32 + row;   // even: f, f+1 are adjacent act columns
                         const uint32_t pk = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
                         // device-coherent store: written through to the memory side, so a down
                         // item on another XCD that reads the row after the counter sees it
@@ -1076,10 +1075,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     } else {
                         const float wv = __int_as_float(tb[128 + tok_i]);
                         float* yr = g.y + (size_t)orow * g.d;
-                        unsafeAtomicAdd(yr + it.abs0 + row, wv * g0);
-                        unsafeAtomicAdd(yr + it.abs0 + row + 1, wv * g1);
-                        unsafeAtomicAdd(yr + it.abs1 + row, wv * u0);
-                        unsafeAtomicAdd(yr + it.abs1 + row + 1, wv * u1);
+                        float* yo = yr + it.tile * 64 + row;   // set 0 rows; set 1 rows 32 further
+                        unsafeAtomicAdd(yo, wv * g0);
+                        unsafeAtomicAdd(yo + 1, wv * g1);
+                        unsafeAtomicAdd(yo + 32, wv * u0);
+                        unsafeAtomicAdd(yo + 33, wv * u1);
                     }
                 }
             }

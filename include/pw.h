@@ -96,8 +96,8 @@ typedef struct {
                               max_tokens*(top_k+1)*max(d_ffn, d_ffn_shared) < 2^31 */
     uint32_t flags;        /* 0, or PW_FLAG_LUT_TILED: every bound LUT page of this layer
                               is in the 32-row tiled order (default: row-major) */
-    int32_t rows_per_block;/* linear-block size: 0 = one block per linear; else a multiple
-                              of 64 dividing d_model, d_ffn and d_ffn_shared, and every
+    int32_t rows_per_block;/* linear-block size: 0 = one block per linear; else a power of
+                              two >= 64 dividing d_model, d_ffn and d_ffn_shared, and every
                               linear is cut into row-blocks of that many rows, each a
                               block with its own bitwidth and pages (legiblepapers "Key
                               Takeaways" and FAQ Q5: bitwidths vary per linear-block) */
