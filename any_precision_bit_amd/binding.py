@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpw.so")
+# PW_LIBRARY names another build of the same ABI (a sanitizer build for host-side tests)
+LIB_PATH = os.environ.get("PW_LIBRARY") or os.path.join(_HERE, "libpw.so")
 
 PW_ABI_VERSION = 2
 PW_FLAG_LUT_TILED = 1

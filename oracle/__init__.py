@@ -24,6 +24,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (a sanitizer build for the pins)
+_LOAD_PATH = os.environ.get("ORACLE_LIBRARY") or _LIB_PATH
 _lib = None
 
 ORC_OK, ORC_E_RANGE, ORC_E_ARG = 0, 1, 2
@@ -40,12 +42,24 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out_dir: str) -> str:
+    """oracle.c with AddressSanitizer and UBSan (gcc) in out_dir; load it with
+    gcc's libasan preloaded and ORACLE_LIBRARY pointing at it."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "liboracle_san.so")
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-fPIC", "-shared", "-o", out, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(_LOAD_PATH)
         P = ctypes.c_void_p
         i32 = ctypes.c_int
         L.orc_router_logits.argtypes = [P, i32, i32, P, i32, P, P]
