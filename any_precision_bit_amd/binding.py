@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PW_OK", 1: "PW_E_ARG", 2: "PW_E_SHAPE", 3: "PW_E_BITS", 4: "
                 5: "PW_E_ALIGN", 6: "PW_E_RANGE", 7: "PW_E_STATE", 8: "PW_E_NOMEM", 9: "PW_E_HIP"}
 EXPORTED = ["pw_layer_create", "pw_layer_destroy", "pw_last_error", "pw_moe_plan_set",
             "pw_page_table_bind", "pw_moe_forward", "pw_layer_status", "pw_moe_replay",
-            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit",
+            "pw_layer_last_bytes", "pw_debug_unpack", "pw_debug_dequant", "pw_debug_set_wait_limit", "pw_debug_set_path",
             "pw_moe_forward_noalloc", "pw_plan_greedy", "pw_page_table_bind_rows"]
 
 
@@ -76,6 +76,7 @@ def _load():
         "pw_debug_unpack": ([P, i32, i32, i32, P, P], st),
         "pw_debug_dequant": ([P, i32, P, u32, i32, i32, P, P], st),
         "pw_debug_set_wait_limit": ([P, u32], st),
+        "pw_debug_set_path": ([P, i32], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -190,3 +191,11 @@ def pw_debug_dequant(planes, b: int, lut: int, R: int, K: int, w_out: int, strea
 
 def pw_debug_set_wait_limit(layer: int, polls: int) -> None:
     _check(lib.pw_debug_set_wait_limit(layer, polls))
+
+
+PATHS = {"auto": 0, "small": 1, "four": 2, "big": 3}
+
+
+def pw_debug_set_path(layer: int, path) -> None:
+    """Which expert kernel takes which experts: 'auto', 'small', 'four', 'big' (or 0..3)."""
+    _check(lib.pw_debug_set_path(layer, PATHS[path] if isinstance(path, str) else int(path)))

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <cstdlib>
 #include <cmath>
 #include <array>
 #include <cstdarg>
@@ -21,6 +23,10 @@
 
 #include "pw.h"
 #include "pw_internal.h"
+
+static_assert(PW_PATH_AUTO == pw::PATH_AUTO && PW_PATH_SMALL == pw::PATH_SMALL && PW_PATH_FOUR == pw::PATH_FOUR &&
+                  PW_PATH_BIG == pw::PATH_BIG,
+              "path values of the ABI and of the launcher");
 
 using pw::DevBlock;
 
@@ -74,6 +80,7 @@ struct DeviceGuard {
 struct pw_launch {
     int T = 0;
     int n_cu = 256;
+    int path = pw::PATH_AUTO;
     pw::RouteParams rp{};
     pw::GemmParams gu{}, dn{};
     const uint16_t* res_x = nullptr;
@@ -114,6 +121,7 @@ struct pw_layer_s {
     // launch record of the last pw_moe_forward (for pw_layer_last_bytes and pw_moe_replay)
     pw_launch rec{};
     uint32_t wait_limit = 1u << 20;   // polls of a down item's dependency counter
+    int path = pw::PATH_AUTO;          // which expert kernel takes which experts (pw::PATH_*)
     // host copy of the page table for pw_moe_forward_noalloc (sized at create)
     std::vector<DevBlock> shadow;
     uint32_t* noalloc_status = nullptr;   // status word in the device scratch, once used
@@ -319,19 +327,38 @@ pw_status upload_tables(pw_layer_s* L, hipStream_t s) {
 }
 
 
+// The expert-kernel path of new layers: PW_FORCE_PATH = auto | small | four | big
+// (read once per process; anything else is auto).
+int default_path() {
+    static const int path = [] {
+        const char* v = getenv("PW_FORCE_PATH");
+        if (!v) return (int)pw::PATH_AUTO;
+        if (!strcmp(v, "small")) return (int)pw::PATH_SMALL;
+        if (!strcmp(v, "four")) return (int)pw::PATH_FOUR;
+        if (!strcmp(v, "big")) return (int)pw::PATH_BIG;
+        return (int)pw::PATH_AUTO;
+    }();
+    return path;
+}
+
 // Kernel arguments of one forward on T tokens with workspace ws, device page
 // table blocks and the shared expert's act rows from shared_base on.
 pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* router_w, const void* router_b,
                       float* y, void* x_next, const pw_route_out* route, const pw::Workspace& ws,
                       const DevBlock* blocks, int shared_base, int n_cu) {
     const pw_moe_desc& D = L->desc;
+    const int path = L->path;
     const int E = D.n_experts, k = D.top_k, d = D.d_model;
     const int has_shared = D.d_ffn_shared > 0;
     const int f_max = std::max(D.d_ffn, D.d_ffn_shared);
     pw_launch r{};
     r.T = T;
     r.n_cu = n_cu;
+    r.path = path;
     pw::RouteParams& rp = r.rp;
+    rp.small_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0 : pw::kSmallMax;
+    rp.four_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0
+                : path == pw::PATH_FOUR ? INT_MAX : (T >= pw::kBigBatch ? pw::kFourMaxBig : pw::kFourMax);
     rp.x = (const uint16_t*)x;
     rp.wr = (const uint16_t*)router_w;
     rp.bias = (const uint16_t*)router_b;
@@ -403,13 +430,20 @@ pw_status launch_phase(const pw_launch& r, int d_model, int phase, hipStream_t s
             pw::ExpertParams ep{r.gu, r.dn};
             ep.gu.list = pw::LIST_GU_SMALL;
             ep.dn.list = pw::LIST_DN_SMALL;
-            if ((e = pw::launch_experts(pw::kSmallTokens, ep, r.n_cu, s)) != hipSuccess)
+            // a kernel is launched when some expert can reach its token range
+            if (r.rp.small_max > 0 && (e = pw::launch_experts(pw::kSmallTokens, ep, r.n_cu, s)) != hipSuccess)
                 return hip_fail(e, "expert kernel");
-            if (T > pw::kSmallMax) {
-                ep.gu.list = pw::LIST_GU_LARGE;
-                ep.dn.list = pw::LIST_DN_LARGE;
+            if (T > r.rp.small_max && r.rp.four_max > r.rp.small_max) {
+                ep.gu.list = pw::LIST_GU_FOUR;
+                ep.dn.list = pw::LIST_DN_FOUR;
                 if ((e = pw::launch_experts(pw::kLargeTokens, ep, r.n_cu, s)) != hipSuccess)
-                    return hip_fail(e, "expert kernel (large)");
+                    return hip_fail(e, "expert kernel (four-tile)");
+            }
+            if (T > r.rp.four_max) {
+                ep.gu.list = pw::LIST_GU_BIG;
+                ep.dn.list = pw::LIST_DN_BIG;
+                if ((e = pw::launch_experts_big(ep, r.n_cu, s)) != hipSuccess)
+                    return hip_fail(e, "expert kernel (dequantise-once)");
             }
             break;
         }
@@ -498,6 +532,7 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     pw_layer_s* L = new (std::nothrow) pw_layer_s();
     if (!L) return fail(PW_E_NOMEM, "pw_layer_create: out of host memory");
     L->desc = D;
+    L->path = default_path();
     L->n_total = D.n_experts + (D.d_ffn_shared > 0 ? 1 : 0);
     make_block_list(L);
     L->pages.resize((size_t)n_blocks(L));
@@ -803,6 +838,14 @@ pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut
 }
 
 }  // extern "C"
+
+pw_status pw_debug_set_path(pw_layer L, int32_t path) {
+    g_err.clear();
+    if (!L) return fail(PW_E_ARG, "pw_debug_set_path: null layer");
+    if (path < PW_PATH_AUTO || path > PW_PATH_BIG) return fail(PW_E_ARG, "path %d not in 0..3", path);
+    L->path = path;
+    return PW_OK;
+}
 
 pw_status pw_debug_set_wait_limit(pw_layer L, uint32_t polls) {
     g_err.clear();

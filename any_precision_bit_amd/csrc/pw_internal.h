@@ -21,7 +21,13 @@ static_assert(sizeof(DevBlock) == 80, "DevBlock layout");
 // expert when there is one, then routed experts 0..E-1), items
 // [prefix[p], prefix[p+1]) belong to that expert; item i of an expert is
 // (row tile i % tiles, token group i / tiles).
-enum { LIST_GU_SMALL = 0, LIST_GU_LARGE = 1, LIST_DN_SMALL = 2, LIST_DN_LARGE = 3, N_LISTS = 4 };
+// Three kernels take an expert by its token count (small: one-tile kernel,
+// four: four-tile kernel, big: dequantise-once kernel), each over a gate_up
+// and a down list.
+enum {
+    LIST_GU_SMALL = 0, LIST_GU_FOUR = 1, LIST_GU_BIG = 2,
+    LIST_DN_SMALL = 3, LIST_DN_FOUR = 4, LIST_DN_BIG = 5, N_LISTS = 6
+};
 
 // Workspace carved out of one device allocation per layer.
 struct Workspace {
@@ -56,6 +62,9 @@ struct RouteParams {
     int pieces_dn_r, pieces_dn_s;           // K-pieces of a routed / the shared down item
     Workspace ws;
     float* y;              // zeroed here
+    int small_max;         // experts with 1..small_max tokens: one-tile lists (16-token groups)
+    int four_max;          // small_max+1..four_max tokens: four-tile lists (64-token groups);
+                           // more: dequantise-once lists (256-token groups)
     int32_t* o_ids;        // optional caller copies of the routing outputs
     float* o_w;
     int32_t* o_counts;
@@ -121,6 +130,8 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s);
 // tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
 // The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s);
+// The dequantise-once kernel over the large lists (groups of kBigTokens tokens).
+hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s);
 // Sets the expert kernels' attributes and caches their per-CU occupancy; the
 // forward calls it before enqueueing anything, so a launch precondition that
 // cannot be met fails the call with nothing enqueued.
@@ -140,7 +151,23 @@ int expert_lds_bytes(int tile_tokens);
 
 constexpr int kSmallTokens = 16;          // token group of the one-tile kernel (one 16-token MFMA tile)
 constexpr int kSmallMax = 32;             // experts with 1..32 tokens: groups of 16 in the one-tile kernel
-constexpr int kLargeTokens = 64;          // larger experts: groups of 64 tokens (four tiles)
+constexpr int kLargeTokens = 64;          // four-tile kernel: groups of 64 tokens
+constexpr int kBigTokens = 256;           // dequantise-once kernel: groups of 256 tokens
+// Experts with 33..kFourMax tokens go to the four-tile kernel (one or two
+// 64-token groups). The dequantise-once kernel has the higher cost per item and
+// pays off once a forward brings it many items: from kBigBatch tokens on, the
+// bound drops to kFourMaxBig (measured crossover on the qwen and fine-grained
+// layers at T = 128 and T = 1024).
+constexpr int kFourMax = 128;
+constexpr int kFourMaxBig = 64;
+constexpr int kBigBatch = 512;
+// Which kernel takes which experts (PW_FORCE_PATH, pw_debug_set_path):
+//   AUTO  1..kSmallMax tokens: one-tile kernel; up to kFourMax (kFourMaxBig when
+//         T >= kBigBatch): four-tile kernel; more: dequantise-once kernel
+//   SMALL every expert in the one-tile kernel (16-token groups)
+//   FOUR  1..kSmallMax: one-tile kernel; more: four-tile kernel (64-token groups)
+//   BIG   every expert in the dequantise-once kernel
+enum { PATH_AUTO = 0, PATH_SMALL = 1, PATH_FOUR = 2, PATH_BIG = 3 };
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
 // act rows of one K-piece start on a 128-byte line (2-byte elements): a line never holds two pieces
 static_assert(kDownPiece % 64 == 0, "K-pieces must start on 128-byte act lines");

@@ -266,7 +266,7 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     // E + 1 positions can exceed the thread count, so they are scanned in chunks
     const int npos = E + p.has_shared;
     const int stride = E + 2;
-    int carry[N_LISTS] = {0, 0, 0, 0};
+    int carry[N_LISTS] = {0, 0, 0, 0, 0, 0};
     for (int p0 = 0; p0 < npos; p0 += kRouteThreads) {
         const int pos = p0 + tid;
         int cnt = 0, tgu = 0, pdn = 1;
@@ -277,13 +277,16 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
             tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
             pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
         }
-        // up to kSmallMax tokens: 16-token groups in the one-tile kernel (at two
-        // work-groups per CU, two such items cost less CU time than one 64-token
-        // item at one work-group per CU); beyond: 64-token groups
-        const int small = (cnt >= 1 && cnt <= kSmallMax) ? (cnt + kSmallTokens - 1) / kSmallTokens : 0;
-        const int groups = cnt > kSmallMax ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
-        const int nitems[N_LISTS] = {small * tgu, groups * tgu, small * p.tiles_dn * pdn,
-                                     groups * p.tiles_dn * pdn};
+        // up to small_max tokens: 16-token groups in the one-tile kernel (at two
+        // work-groups per CU, two such items cost less CU time than one item of
+        // a large kernel at one work-group per CU); up to four_max: 64-token
+        // groups in the four-tile kernel; beyond: 256-token groups in the
+        // dequantise-once kernel
+        const int small = (cnt >= 1 && cnt <= p.small_max) ? (cnt + kSmallTokens - 1) / kSmallTokens : 0;
+        const int four = (cnt > p.small_max && cnt <= p.four_max) ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
+        const int big = cnt > p.four_max ? (cnt + kBigTokens - 1) / kBigTokens : 0;
+        const int tdn = p.tiles_dn * pdn;
+        const int nitems[N_LISTS] = {small * tgu, four * tgu, big * tgu, small * tdn, four * tdn, big * tdn};
         int ex[N_LISTS], tot[N_LISTS];
         block_excl_scan_n<N_LISTS>(nitems, s_tmp, ex, tot);
 #pragma unroll
@@ -1112,6 +1115,369 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
     }
 }
 
+// ============================================================================ dequantise-once kernel
+
+// Experts with many tokens: each weight of an item is dequantised once and
+// multiplied with up to kBigTokens tokens (legiblepapers FAQ Q5: the fused
+// kernel reads the planes and LUTs directly; here the per-weight unpack and
+// lookup cost is shared by all of an item's tokens instead of being repeated
+// per 64-token group).
+//
+// Work-group of 8 waves, one per CU. Items are those of the large lists, with
+// the same rows and K ranges as in expert_kernel (gate_up: 32 rows of gate and
+// of up; down: 64 rows, one K-piece) and up to 256 tokens each.
+//   - Waves 0..3 (producers) unpack and look up exactly as expert_kernel does
+//     (wave q: rows 16*(q >> 1) .. +15, half-line q & 1; lane (r, kg)), but
+//     write the looked-up weights to LDS instead of multiplying them. One step
+//     is one 32-column dword of every lane: 64 rows x 256 columns, 32 KiB, laid
+//     out as 32 MFMA A fragments (16 rows x 32 columns, 1 KiB each) whose 32
+//     columns are contiguous: fragment (set, row half, kh, kg) holds columns
+//     kh*512 + kg*128 + 32*dw + [0, 32) of the chunk, lane (r, kq) of it the
+//     eight columns 8*kq .. +7 (the producer's lookup step m = kq).
+//   - Waves 4..7 (consumers) take 64 tokens each (four 16-token MFMA tiles)
+//     and multiply every fragment of a step with their tokens' activation
+//     fragments (x rows or act rows, loaded straight from L2: per token 64
+//     contiguous bytes per fragment, 16 rows per load instruction),
+//     accumulating the whole item (64 rows x 64 tokens) in registers; the
+//     epilogue is expert_kernel's (SwiGLU -> act, or w * o added into y).
+// Steps are pipelined through two 32 KiB buffers: in phase f the producers
+// write step f into buffer f & 1 while the consumers read step f - 1 from the
+// other, and a work-group barrier ends every phase. A producer item starts by
+// writing its LUT rows to the stripe, which every producer has stopped reading
+// at the previous phase's barrier; a second barrier then publishes them. The
+// consumer walks the same item sequence one step behind and executes the same
+// barriers. The item order, the dependency counters (one increment per
+// consumer wave, after its act stores have drained) and the deadlock argument
+// are those of expert_kernel.
+constexpr int kBigWaves = 8;
+constexpr int kWStepBytes = 32 * 1024;
+
+__device__ __forceinline__ int w_frag(int s, int rh, int kh, int kg) { return ((s * 2 + rh) * 2 + kh) * 4 + kg; }
+
+__global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NT = kBigTokens / 16;   // token tiles per item (decode_item's group size)
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    unsigned char* wbuf = smem + kStripeBytes;                    // [2][32 fragments][64 lanes][16 B]
+    int* s_pre = (int*)(wbuf + 2 * kWStepBytes);                  // [2][kPreWords]: gate_up, down
+    int* s_flag = s_pre + 2 * kPreWords;
+    uint32_t* s_ready = (uint32_t*)(s_flag + 1);                  // last down item whose act rows are ready
+    const GemmParams& g = p.gu;
+    uint32_t* const dep = g.ws.dep;
+    const int dstride = g.ws.dep_stride;
+    const int npos = g.E + g.has_shared;
+    for (int i = tid; i <= npos; i += kBigWaves * 64) {
+        s_pre[i] = g.ws.prefix[p.gu.list * (g.E + 2) + i];
+        s_pre[kPreWords + i] = g.ws.prefix[p.dn.list * (g.E + 2) + i];
+    }
+    if (tid == 0) *s_ready = 0u;
+    __syncthreads();
+    const int n_gu = __builtin_amdgcn_readfirstlane(s_pre[npos]);
+    const int n_items = n_gu + __builtin_amdgcn_readfirstlane(s_pre[kPreWords + npos]);
+    auto decode = [&](int i) -> Item {
+        return i < n_gu ? decode_item<0, NT>(p.gu, s_pre, npos, i)
+                        : decode_item<1, NT>(p.dn, s_pre + kPreWords, npos, i - n_gu);
+    };
+    auto n_steps = [](const Item& it) { return 4 * ((it.klen + 1023) >> 10); };
+
+    if (wave < 4 && (int)blockIdx.x < n_items) {
+        // ------------------------------------------------------------ producers
+        int r = tid & 15, kg = (tid >> 4) & 3;
+        const int rh = wave >> 1, kh = wave & 1;
+        uint4 pa0[8], pa1[8], pb0[8], pb1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pa0[i] = pa1[i] = pb0[i] = pb1[i] = make_uint4(0, 0, 0, 0);
+        auto lane_col = [&](int ch) { return ch * 1024 + kh * 512 + kg * 128; };
+        auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
+            const int Kb = it.K >> 3;
+            const bool vg = lane_col(ch) < it.klen;
+            const uint32_t nrec = (uint32_t)(it.R * Kb);
+            const int cb = (it.kbase + lane_col(ch)) >> 3;
+            const int row = rh * 16 + r;
+            const uint32_t off0 = vg ? (uint32_t)((it.rows0 + row) * Kb + cb) : kOOB;
+            const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
+            const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
+                c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
+            }
+        };
+        auto lut_load = [&](const Item& it, LutStage& st) {
+            const int b0 = it.blk0->bits, b1 = it.blk1->bits;
+            lut_stage_load(st, (const uint16_t*)it.blk0->lut + ((size_t)it.rows0 << b0), b0,
+                           (const uint16_t*)it.blk1->lut + ((size_t)it.rows1 << b1), b1, tid, g.lut_tiled);
+        };
+        int item = blockIdx.x;
+        Item it = decode(item);
+        LutStage st;
+        load_chunk(it, 0, pa0, pa1);
+        lut_load(it, st);
+        while (true) {
+            asm volatile("" : "+v"(r), "+v"(kg));
+            lut_stage_write(smem, st, it.blk0->bits, it.blk1->bits, tid);
+            __syncthreads();   // the item's LUT rows are in the stripe
+            const int nch = (it.klen + 1023) >> 10;
+            const int next = item + (int)gridDim.x;
+            const bool has_next = next < n_items;
+            Item nit = it;
+            if (has_next) nit = decode(next);
+            const uint32_t slot = lds_addr(smem) + (uint32_t)((rh * 32 + (kg & 1) * 16 + r) * 4);
+            // lookup step m of lane (r, kg) is lane (r, kq = m) of fragment kg
+            unsigned char* wl = wbuf + r * 16;
+            auto produce = [&](int ch, int dw, const uint4 (&c0)[8], const uint4 (&c1)[8], int buf) {
+                if (ch * 1024 + kh * 512 >= it.klen) return;   // this wave's half-chunk lies past K
+                uint32_t w0[8], w1[8], rw0[8], rw1[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    w0[i] = word_of(c0[i], dw);
+                    w1[i] = word_of(c1[i], dw);
+                }
+                slots_to_indices(w0, rw0);
+                slots_to_indices(w1, rw1);
+                unsigned char* wb = wl + buf * kWStepBytes;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const half8 a0 = lut_fragment(rw0, m, slot, 0);
+                    const half8 a1 = lut_fragment(rw1, m, slot, 2);
+                    *(half8*)(wb + w_frag(0, rh, kh, kg) * 1024 + m * 256) = a0;
+                    *(half8*)(wb + w_frag(1, rh, kh, kg) * 1024 + m * 256) = a1;
+                }
+            };
+            bool fetched = false;
+            auto fetch_next = [&]() {
+                if (has_next) {
+                    load_chunk(nit, 0, pa0, pa1);
+                    lut_load(nit, st);
+                }
+                fetched = true;
+            };
+            // global step parity: the consumers read buffer (step & 1) one phase later
+            if (1 < nch) load_chunk(it, 1, pb0, pb1);
+#pragma unroll 1
+            for (int ch = 0; ch < nch; ch += 2) {
+#pragma unroll
+                for (int dw = 0; dw < 4; ++dw) {
+                    produce(ch, dw, pa0, pa1, dw & 1);
+                    __syncthreads();   // step published; the other buffer has been read
+                }
+                if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
+                else if (ch + 1 < nch) fetch_next();
+                if (ch + 1 >= nch) break;
+#pragma unroll
+                for (int dw = 0; dw < 4; ++dw) {
+                    produce(ch + 1, dw, pb0, pb1, dw & 1);
+                    __syncthreads();
+                }
+                if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
+            }
+            if (!fetched) fetch_next();
+            if (!has_next) break;
+            item = next;
+            it = nit;
+        }
+    } else if (wave >= 4 && (int)blockIdx.x < n_items) {
+        // ------------------------------------------------------------ consumers
+        const int cw = wave - 4;              // tokens 64*cw .. +63 of the item
+        const int tr = lane & 15, kq = lane >> 4;
+        int item = blockIdx.x;
+        Item it = decode(item);
+        // phase 0: the producers' first step (the first item's stripe write, then the step)
+        __syncthreads();
+        __syncthreads();
+        while (true) {
+            const int S = n_steps(it);
+            const int next = item + (int)gridDim.x;
+            const bool has_next = next < n_items;
+            const int ldb = it.mode == 0 ? g.d : g.ld_act;
+            const __amdgpu_buffer_rsrc_t brsrc =
+                it.mode == 0 ? make_rsrc(g.x, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
+            // this wave's tokens: B row, output row and weight of token 64*cw + 16*t + tr
+            const bool sh = it.ex == g.E;
+            const int obase = sh ? 0 : kconst(g.ws.offsets)[it.ex];
+            int ntl = (it.nl - 64 * cw + 15) >> 4;
+            ntl = ntl < 0 ? 0 : (ntl > 4 ? 4 : ntl);
+            uint32_t boff[4];
+            int orow[4];
+            float wt[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int li = 64 * cw + 16 * t + tr;
+                boff[t] = kOOB;
+                orow[t] = -1;
+                wt[t] = 0.0f;
+                if (li < it.nl) {
+                    const int tkn = it.tbase + li;
+                    const int slotn = sh ? (g.shared_base + tkn) : (obase + tkn);
+                    const int tok = sh ? tkn : g.ws.slot_tok[slotn];
+                    const int brow = it.mode == 0 ? tok : slotn;
+                    orow[t] = it.mode == 0 ? slotn : tok;
+                    wt[t] = (it.mode == 0 || sh) ? 1.0f : g.ws.slot_w[slotn];
+                    boff[t] = (uint32_t)(brow * ldb + kq * 8);
+                }
+            }
+            if (it.mode == 1) {
+                // every gate_up item of this expert's K-piece has released its act rows:
+                // the first consumer wave polls the counter (one poller per work-group,
+                // spaced out, keeps the polls off the memory system) and publishes the
+                // item in LDS; the other consumer waves wait for that, and none of them
+                // loads act before (the dependency invariants of expert_kernel)
+                if (cw == 0) {
+                    const uint32_t need =
+                        (uint32_t)((it.klen >> 5) * ((it.n_tok + kBigTokens - 1) / kBigTokens) * 4);
+                    const uint32_t* c = dep + it.pos * dstride + it.piece;
+                    uint32_t polls = 0;
+                    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                        if (polls++ >= kconst(g.ws.wait_limit)[0]) {
+                            if (lane == 0) atomicOr(g.ws.status, PW_STATUS_DEP_TIMEOUT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(4);
+                    }
+                    __hip_atomic_store(s_ready, (uint32_t)item + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                } else {
+                    // ends once wave 4 has published this item (its own wait is bounded)
+                    while (__hip_atomic_load(s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != (uint32_t)item + 1u)
+                        __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            floatx4 acc[2][2][4];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[s][h][t] = (floatx4)0.0f;
+            // B fragments of half kh of step sc: tile t, fragment kg (columns
+            // kh*512 + kg*128 + 32*dw + [0, 32) of chunk sc >> 2; lane (tok, kq): 8 of them)
+            auto kvalid = [&](int sc, int kh, int kg) { return (sc >> 2) * 1024 + kh * 512 + kg * 128 < it.klen; };
+            // Every call issues its 16 loads (inactive ones read zeros without touching
+            // memory), so the loads in flight are the same on every path and the
+            // waits before the MFMAs count exactly: a conditional prefetch would
+            // make them wait for it too.
+            auto load_b = [&](int sc, int kh, half8 (&bq)[4][4], bool on) {
+                const int col = (sc >> 2) * 1024 + kh * 512 + (sc & 3) * 32;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) {
+                        // a select, not a branch: no short-circuit evaluation
+                        const bool ok = on & kvalid(sc, kh, kg) & (t < ntl) & (boff[t] != kOOB);
+                        const uint32_t off = ok ? (boff[t] + (uint32_t)(it.kbase + col + kg * 128)) * 2u : kOOB;
+                        bq[t][kg] = __builtin_bit_cast(half8, buf_load16(brsrc, off));
+                    }
+            };
+            // All four tiles of a wave with tokens: tiles and lanes without a token
+            // hold zero B fragments (per-tile guards would split every MFMA into
+            // its own basic block and serialise the fragment reads).
+            // The fragments of k-block kg + 1 are read before the MFMAs of kg, so
+            // the LDS latency overlaps the matrix work. Fragments past K are never
+            // multiplied (their B fragments are zero anyway).
+            auto mma = [&](int sc, int kh, const half8 (&bq)[4][4]) {
+                if (ntl == 0) return;
+                const unsigned char* wb = wbuf + (sc & 1) * kWStepBytes + lane * 16;
+                half8 a[2][2][2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) a[0][s][h] = *(const half8*)(wb + w_frag(s, h, kh, 0) * 1024);
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) {
+                    if (kg < 3) {
+#pragma unroll
+                        for (int s = 0; s < 2; ++s)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                a[(kg + 1) & 1][s][h] = *(const half8*)(wb + w_frag(s, h, kh, kg + 1) * 1024);
+                    }
+                    if (!kvalid(sc, kh, kg)) continue;   // columns past K (uniform)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                acc[s][h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kg & 1][s][h], bq[t][kg], acc[s][h][t], 0, 0, 0);
+                }
+            };
+            half8 bq0[4][4], bq1[4][4];
+            load_b(0, 0, bq0, true);
+#pragma unroll 1
+            for (int sc = 0; sc < S; ++sc) {
+                load_b(sc, 1, bq1, true);
+                mma(sc, 0, bq0);
+                load_b(sc + 1, 0, bq0, sc + 1 < S);   // the next step's first half (none after the last)
+                mma(sc, 1, bq1);
+                if (sc + 1 == S) {
+                    // epilogue: the item is complete in this wave's registers
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            if (t >= ntl || orow[t] < 0) continue;
+                            const int row = h * 16 + kq * 4;   // rows row .. row+3 of the set
+                            if (it.mode == 0) {
+                                uint32_t pk[2];
+#pragma unroll
+                                for (int j = 0; j < 2; ++j) {
+                                    const float g0 = acc[0][h][t][2 * j], u0 = acc[1][h][t][2 * j];
+                                    const float g1 = acc[0][h][t][2 * j + 1], u1 = acc[1][h][t][2 * j + 1];
+                                    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
+                                    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
+                                    pk[j] = (uint32_t)f2h(a0) | ((uint32_t)f2h(a1) << 16);
+                                }
+                                const uint64_t v = (uint64_t)pk[0] | ((uint64_t)pk[1] << 32);
+                                // device-coherent store (written through), drained before the counter
+                                __hip_atomic_store((uint64_t*)(g.ws.act + (size_t)orow[t] * g.ld_act + it.tile * 32 + row),
+                                                   v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            } else {
+                                float* yo = g.y + (size_t)orow[t] * g.d + it.tile * 64 + row;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    unsafeAtomicAdd(yo + i, wt[t] * acc[0][h][t][i]);
+                                    unsafeAtomicAdd(yo + 32 + i, wt[t] * acc[1][h][t][i]);
+                                }
+                            }
+                        }
+                    if (it.mode == 0) {
+                        vm_drain();   // this wave's act stores are complete
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(dep + it.pos * dstride + ((it.tile * 32) / kDownPiece), 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                // the producers' step sc + 1 of this item, or the next item's first step
+                // (LUT stripe write and its barrier first), in the same phase
+                if (sc + 1 < S) {
+                    __syncthreads();
+                } else if (has_next) {
+                    __syncthreads();
+                    __syncthreads();
+                }
+            }
+            if (!has_next) break;
+            item = next;
+            it = decode(item);
+        }
+    }
+
+    // the last work-group to finish zeroes the dependency counters
+    __syncthreads();
+    if (tid == 0) {
+        vm_drain();
+        const uint32_t prev = __hip_atomic_fetch_add(dep + (size_t)npos * dstride, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == gridDim.x - 1u;
+    }
+    __syncthreads();
+    if (*s_flag) {
+        for (int i = tid; i <= npos * dstride; i += kBigWaves * 64)
+            __hip_atomic_store(dep + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // ============================================================================ residual / init / debug
 
 __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const float* y,
@@ -1279,12 +1645,46 @@ static hipError_t launch_experts_t(const ExpertParams& p, int n_cu, hipStream_t 
     return hipGetLastError();
 }
 
+static int big_lds_bytes() { return kStripeBytes + 2 * kWStepBytes + 2 * kPreWords * 4 + 16; }   // + flag, ready
+
+// Resident work-groups per CU of the dequantise-once kernel (at most 1).
+static hipError_t big_occupancy(int* per_cu) {
+    static int cached = -1;
+    if (cached < 0) {
+        const void* f = (const void*)expert_kernel_big;
+        hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (err != hipSuccess) return err;
+        int n = 0;
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kBigWaves * 64, big_lds_bytes());
+        if (err != hipSuccess) return err;
+        cached = n < 1 ? n : 1;
+    }
+    *per_cu = cached;
+    return hipSuccess;
+}
+
+hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s) {
+    int per_cu = 0;
+    hipError_t err = big_occupancy(&per_cu);
+    if (err != hipSuccess) return err;
+    if (per_cu < 1) return hipErrorLaunchOutOfResources;
+    if (cooperative_launch()) {
+        ExpertParams arg = p;
+        void* args[] = {(void*)&arg};
+        return hipLaunchCooperativeKernel((const void*)expert_kernel_big, dim3(per_cu * n_cu), dim3(kBigWaves * 64),
+                                          args, (unsigned)big_lds_bytes(), s);
+    }
+    hipLaunchKernelGGL(expert_kernel_big, dim3(per_cu * n_cu), dim3(kBigWaves * 64), big_lds_bytes(), s, p);
+    return hipGetLastError();
+}
+
 hipError_t prepare_experts() {
-    int a = 0, b = 0;
+    int a = 0, b = 0, c = 0;
     hipError_t err = expert_occupancy<1>(&a);
     if (err == hipSuccess) err = expert_occupancy<4>(&b);
+    if (err == hipSuccess) err = big_occupancy(&c);
     if (err != hipSuccess) return err;
-    return (a < 1 || b < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
+    return (a < 1 || b < 1 || c < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
 }
 
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {

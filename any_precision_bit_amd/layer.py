@@ -91,6 +91,10 @@ class PagedMoELayer:
         """Test hook: polls of a down item's dependency counter before it gives up."""
         B.pw_debug_set_wait_limit(self.handle, polls)
 
+    def set_path(self, path) -> None:
+        """A/B switch of the expert kernels: 'auto', 'small', 'four' or 'big'."""
+        B.pw_debug_set_path(self.handle, path)
+
     def last_bytes(self, stream: Optional[torch.cuda.Stream] = None):
         s = stream if stream is not None else torch.cuda.current_stream()
         return B.pw_layer_last_bytes(self.handle, int(s.cuda_stream))

@@ -66,25 +66,29 @@ def check_routing(route, ref, T, E, k):
 
 
 def run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=None, pages=None, lut_tiled=False,
-               max_tokens=None):
+               max_tokens=None, path=None, ref=None):
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
     T = x.shape[0]
     pages = pages or device_pages(blocks, bits, dev, lut_tiled=lut_tiled)
     lay = layer or gpu_layer(cfg, bits, pages, max_tokens=max_tokens or T, lut_tiled=lut_tiled)
+    if path is not None:
+        lay.set_path(path)
     xd, wd = to_dev_f16(x, dev), to_dev_f16(wr, dev)
     bd = None if bias is None else to_dev_f16(bias, dev)
     route = route_buffers(T, cfg.E, cfg.k, dev)
     y = lay.forward(xd, wd, bd, route=route)
     torch.cuda.synchronize()
     assert lay.status() == 0
-    ref = oracle.OracleLayer.from_config(cfg, bits, blocks, rows_per_block=lay.rows_per_block).forward(
-        x, wr, bias, subset=subset)
+    if ref is None:
+        ref = oracle.OracleLayer.from_config(cfg, bits, blocks, rows_per_block=lay.rows_per_block).forward(
+            x, wr, bias, subset=subset)
     check_routing(route, ref, T, cfg.E, cfg.k)
     yh = y.cpu().numpy()
     err = rel_err_per_token(yh[subset], ref["y"][subset])
-    _say(f"{cfg.name} T={T}: max rel err {err.max():.3e} over {len(subset)} tokens")
+    _say(f"{cfg.name} T={T}{'' if path is None else ' path=' + str(path)}: max rel err {err.max():.3e} "
+         f"over {len(subset)} tokens")
     assert err.max() <= REL_TOL
     return lay, y, ref
 
@@ -139,6 +143,33 @@ def test_fine_e128(torch_dev):
     blocks = _blocks(cfg, bits)
     _, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
     assert ref["counts"].max() > 32          # exercises the multi-tile (large) kernels
+
+
+@pytest.mark.parametrize("name,T", [("tiny_d256", 200), ("fine_e128_t128", 128), ("qwen_d2048_t16", 300)])
+def test_expert_paths(torch_dev, name, T):
+    """Every A/B path of the expert kernels on the same layer and batch: the one-tile kernel alone,
+    the four-tile kernel for experts above 32 tokens, the dequantise-once kernel for them (the
+    default) and for every expert. T = 300 puts the qwen shared expert in two 256-token passes
+    (a ragged 44-token second pass); tiny_d256 and fine_e128_t128 have routed experts above 32
+    tokens."""
+    cfg = synth.CONFIGS[name].with_tokens(T)
+    _say(f"{name} T={T}: expert paths")
+    x, wr, bias = layer_inputs(cfg)
+    L, _ = oracle.router_logits(x, wr, bias)
+    ids, _ = oracle.topk_softmax(L, cfg.k)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    bits = synth.initial_bits(cfg, counts=counts) if name == "fine_e128_t128" else synth.initial_bits(cfg)
+    blocks = _blocks(cfg, bits)
+    if T <= 200:
+        subset = np.arange(T, dtype=np.int32)
+    else:   # tokens of the largest routed experts, and both shared-expert passes
+        big = np.argsort(-counts, kind="stable")[:3]
+        toks = np.unique(np.nonzero(np.isin(ids, big))[0])
+        subset = np.unique(np.concatenate([toks[:12], np.arange(0, T, 23), [T - 1]])).astype(np.int32)
+    assert counts.max() > 32 or (cfg.Fs > 0 and T > 256)
+    lay, ref = None, None
+    for path in ["auto", "small", "four", "big"]:
+        lay, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=lay, path=path, ref=ref)
 
 
 def _rewrite_all(cfg, layers, s):
