@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("PW_LIBRARY") or os.path.join(_HERE, "libpw.so")
 
 PW_ABI_VERSION = 2
 PW_FLAG_LUT_TILED = 1
+PW_FLAG_DETERMINISTIC = 2
 PW_GATE, PW_UP, PW_DOWN = 0, 1, 2
 PW_STATUS_ROUTER_RANGE = 1
 PW_STATUS_DEP_TIMEOUT = 2

@@ -90,7 +90,8 @@ struct pw_launch {
 
 // Byte offsets of the workspace arrays for forwards of up to T tokens.
 struct WsLayout {
-    size_t o_ids, o_w, o_cnt, o_off, o_srt, o_stk, o_sw, o_pre, o_act, o_st, o_lg, o_dep, total;
+    size_t o_ids, o_w, o_cnt, o_off, o_srt, o_inv, o_stk, o_sw, o_pre, o_act, o_part, o_st, o_lg, o_dep, total;
+    bool det;
     int T, n_dep, n_counters, dep_stride;
 };
 
@@ -192,6 +193,13 @@ void release_device(pw_layer_s* L) {
     L->dev_ready = false;
 }
 
+// K-pieces of a routed / the shared down projection
+int pieces_routed(const pw_moe_desc& D) { return (D.d_ffn + pw::kDownPiece - 1) / pw::kDownPiece; }
+int pieces_shared(const pw_moe_desc& D) { return (D.d_ffn_shared + pw::kDownPiece - 1) / pw::kDownPiece; }
+size_t part_rows(const pw_moe_desc& D, int T) {
+    return (size_t)T * D.top_k * pieces_routed(D) + (size_t)T * pieces_shared(D);
+}
+
 WsLayout ws_layout(const pw_moe_desc& D, int T) {
     const int E = D.n_experts, k = D.top_k;
     const int has_shared = D.d_ffn_shared > 0;
@@ -205,10 +213,15 @@ WsLayout ws_layout(const pw_moe_desc& D, int T) {
     w.o_cnt = off;    off += al(sizeof(int32_t) * (size_t)E);
     w.o_off = off;    off += al(sizeof(int32_t) * ((size_t)E + 1));
     w.o_srt = off;    off += al(sizeof(int32_t) * (size_t)T * k);
+    w.o_inv = off;    off += al(sizeof(int32_t) * (size_t)T * k);
     w.o_stk = off;    off += al(sizeof(int32_t) * (size_t)T * k);
     w.o_sw = off;     off += al(sizeof(float) * (size_t)T * k);
     w.o_pre = off;    off += al(sizeof(int32_t) * (size_t)pw::N_LISTS * (E + 2));
     w.o_act = off;    off += al(sizeof(uint16_t) * act_rows * (size_t)f_max);
+    // deterministic mode: one fp32 row of d per (routed slot, K-piece) and per (token, shared K-piece)
+    w.det = (D.flags & PW_FLAG_DETERMINISTIC) != 0;
+    w.o_part = off;
+    if (w.det) off += al(sizeof(float) * part_rows(D, T) * (size_t)D.d_model);
     w.o_st = off;     off += al(2 * sizeof(uint32_t));   // status, wait limit
     w.o_lg = off;     off += al(sizeof(long long) * (size_t)T * E);
     w.dep_stride = (f_max + pw::kDownPiece - 1) / pw::kDownPiece;
@@ -228,6 +241,8 @@ pw::Workspace carve(char* b, const WsLayout& w) {
     ws.counts = (int32_t*)(b + w.o_cnt);
     ws.offsets = (int32_t*)(b + w.o_off);
     ws.sorted = (int32_t*)(b + w.o_srt);
+    ws.slot_of = (int32_t*)(b + w.o_inv);
+    ws.part = w.det ? (float*)(b + w.o_part) : nullptr;
     ws.slot_tok = (int32_t*)(b + w.o_stk);
     ws.slot_w = (float*)(b + w.o_sw);
     ws.prefix = (int32_t*)(b + w.o_pre);
@@ -356,6 +371,7 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     r.n_cu = n_cu;
     r.path = path;
     pw::RouteParams& rp = r.rp;
+    rp.exact_all = T <= pw::kRouteExactAllMax ? 1 : 0;
     rp.small_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0 : pw::kSmallMax;
     rp.four_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0
                 : path == pw::PATH_FOUR ? INT_MAX : (T >= pw::kBigBatch ? pw::kFourMaxBig : pw::kFourMax);
@@ -394,6 +410,8 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     gp.ld_act = f_max;
     gp.shared_base = shared_base;
     gp.lut_tiled = (D.flags & PW_FLAG_LUT_TILED) ? 1 : 0;
+    gp.det = (D.flags & PW_FLAG_DETERMINISTIC) ? 1 : 0;
+    gp.part_shared = T * k * pieces_routed(D);
     gp.rb_lg = 0;
     while (D.rows_per_block > 0 && (1 << gp.rb_lg) < D.rows_per_block) ++gp.rb_lg;
     gp.y = y;
@@ -445,6 +463,10 @@ pw_status launch_phase(const pw_launch& r, int d_model, int phase, hipStream_t s
                 if ((e = pw::launch_experts_big(ep, r.n_cu, s)) != hipSuccess)
                     return hip_fail(e, "expert kernel (dequantise-once)");
             }
+            if (r.dn.det && (e = pw::launch_reduce(r.dn.ws, r.dn.y, T, r.dn.k, r.dn.d, r.dn.pieces_r,
+                                                    r.dn.has_shared ? r.dn.pieces_s : 0, r.dn.part_shared, s)) !=
+                                hipSuccess)
+                return hip_fail(e, "reduce kernel");
             break;
         }
         case 2:
@@ -505,7 +527,8 @@ pw_status pw_layer_create(const pw_moe_desc* desc, pw_layer* out) {
     const pw_moe_desc& D = *desc;
     if (D.abi_version != PW_ABI_VERSION)
         return fail(PW_E_ARG, "abi_version %d, library is %d", D.abi_version, PW_ABI_VERSION);
-    if (D.flags & ~PW_FLAG_LUT_TILED) return fail(PW_E_ARG, "flags 0x%x: only PW_FLAG_LUT_TILED is defined", D.flags);
+    if (D.flags & ~(PW_FLAG_LUT_TILED | PW_FLAG_DETERMINISTIC))
+        return fail(PW_E_ARG, "flags 0x%x: only PW_FLAG_LUT_TILED and PW_FLAG_DETERMINISTIC are defined", D.flags);
     if (D.rows_per_block < 0 || D.rows_per_block % 64 || (D.rows_per_block & (D.rows_per_block - 1)) ||
         (D.rows_per_block > 0 && (D.d_model % D.rows_per_block || D.d_ffn % D.rows_per_block ||
                                   D.d_ffn_shared % D.rows_per_block)))
@@ -639,7 +662,7 @@ pw_status pw_moe_forward(pw_layer L, const void* x, int32_t T, const void* route
     hipStream_t s = (hipStream_t)stream;
     // every launch precondition (kernel attributes, occupancy) before the first enqueue
     {
-        const hipError_t e = pw::prepare_experts();
+        const hipError_t e = pw::prepare_experts((L->desc.flags & PW_FLAG_DETERMINISTIC) != 0);
         if (e != hipSuccess) return hip_fail(e, "expert kernel set-up");
     }
     if ((st = ensure_device(L, s)) != PW_OK) return st;
@@ -673,7 +696,7 @@ pw_status pw_moe_forward_noalloc(pw_layer L, const void* x, int32_t T, const voi
     size_t cap = 0;
     hipError_t e = pw::scratch_memory(L->device, (void**)&scratch, &cap);
     if (e != hipSuccess) return hip_fail(e, "device scratch address");
-    if ((e = pw::prepare_experts()) != hipSuccess) return hip_fail(e, "expert kernel set-up");
+    if ((e = pw::prepare_experts((L->desc.flags & PW_FLAG_DETERMINISTIC) != 0)) != hipSuccess) return hip_fail(e, "expert kernel set-up");
     int n_cu = 0;
     if ((st = device_cus(L->device, &n_cu)) != PW_OK) return st;
     DevBlock* d_blocks = (DevBlock*)scratch;

@@ -36,6 +36,9 @@ struct Workspace {
     int32_t* counts;     // [E]
     int32_t* offsets;    // [E+1]
     int32_t* sorted;     // [max_T*k]    assignment t*k+j, grouped by expert
+    int32_t* slot_of;    // [max_T*k]    sorted position of assignment t*k+j (inverse of sorted)
+    float* part;         // [max_T*k*pieces_r + max_T*pieces_s][d]  deterministic mode only (else null):
+                         //              each down item's weighted output rows, summed by reduce_kernel
     int32_t* slot_tok;   // [max_T*k]    token t of each sorted slot
     float* slot_w;       // [max_T*k]    routing weight of each sorted slot
     int32_t* prefix;     // [N_LISTS][E+2]
@@ -62,6 +65,8 @@ struct RouteParams {
     int pieces_dn_r, pieces_dn_s;           // K-pieces of a routed / the shared down item
     Workspace ws;
     float* y;              // zeroed here
+    int exact_all;         // 1: exact logits of every expert in the first pass (small T); 0: fp32
+                           // bounds first, exact logits of the candidates only
     int small_max;         // experts with 1..small_max tokens: one-tile lists (16-token groups)
     int four_max;          // small_max+1..four_max tokens: four-tile lists (64-token groups);
                            // more: dequantise-once lists (256-token groups)
@@ -92,6 +97,8 @@ struct GemmParams {
     Workspace ws;
     int ld_act;               // row stride of act (F_max)
     int shared_base;          // first act row of the shared expert (max_T*k)
+    int det;                  // deterministic accumulation: down items write ws.part rows
+    int part_shared;          // first ws.part row of the shared expert (T*k*pieces_r)
     int lut_tiled;            // LUT pages in the 32-row tiled order (else row-major)
     int rb_lg;                // log2 of the rows per linear-block (0: whole linears); blocks
                               // are numbered expert, linear, row-block
@@ -135,9 +142,13 @@ hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s);
 // Sets the expert kernels' attributes and caches their per-CU occupancy; the
 // forward calls it before enqueueing anything, so a launch precondition that
 // cannot be met fails the call with nothing enqueued.
-hipError_t prepare_experts();
+hipError_t prepare_experts(bool det);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,
                            hipStream_t s);
+// Deterministic mode: y[t] = sum over j < k, piece < pr of part[slot_of[t*k+j]*pr + piece]
+// + sum over piece < ps of part[part_shared + t*ps + piece], in that order.
+hipError_t launch_reduce(const Workspace& ws, float* y, int T, int k, int d, int pr, int ps, int part_shared,
+                         hipStream_t s);
 hipError_t launch_debug(const uint64_t* planes8, int b, const uint16_t* lut, int lut_tiled, int R, int K,
                         uint8_t* idx_out, uint16_t* w_out, hipStream_t s);
 
@@ -172,7 +183,9 @@ constexpr int kDownPiece = 2048;          // K columns of one down item (partial
 // act rows of one K-piece start on a 128-byte line (2-byte elements): a line never holds two pieces
 static_assert(kDownPiece % 64 == 0, "K-pieces must start on 128-byte act lines");
 constexpr int kRouteThreads = 256;          // route kernel: 4 waves
-constexpr int kRouteExpertsPerWave = 2;     // router rows per wave
+constexpr int kRouteFilterPerWave = 4;      // router rows per wave in the fp32 pass
+constexpr int kRouteExactPerWave = 2;       // router rows per wave when every logit is exact
+constexpr int kRouteExactAllMax = 32;       // T up to which every logit is computed exactly
 constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)
 
 }  // namespace pw

@@ -255,6 +255,7 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
         if (valid) {
             const int pos = s_wc[wave * E + e] + rank;
             p.ws.sorted[pos] = i;
+            p.ws.slot_of[i] = pos;
             p.ws.slot_tok[pos] = i / p.k;   // token of the slot, and its routing weight
             p.ws.slot_w[pos] = load_agent(p.ws.w + i);
             if (p.o_sorted) p.o_sorted[pos] = i;
@@ -301,37 +302,35 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     }
 }
 
-// Exact router logits of kRouteExpertsPerWave experts e0, e0 + 1, ... for token
-// t, one wave (lane l takes columns l*8 + 512*i, four 512-column blocks per
-// batch, all loads of a batch issued first): int64 sums in units of 2^-48,
-// with sum |x w| and the out-of-range flag of each.
-__device__ __forceinline__ void exact_logits(const RouteParams& p, int t, int e0, int lane,
-                                             long long (&acc)[kRouteExpertsPerWave],
-                                             float (&sab)[kRouteExpertsPerWave], int (&bad)[kRouteExpertsPerWave]) {
-    constexpr int EW = kRouteExpertsPerWave;
+// Exact router logits of the experts ex[0], ex[1] (-1: none) for token t, one
+// wave (lane l takes columns l*8 + 512*i, four 512-column blocks per batch, all
+// loads of a batch issued first): int64 sums in units of 2^-48, with sum |x w|
+// and the out-of-range flag of each.
+__device__ __forceinline__ void exact_logits(const RouteParams& p, int t, const int (&ex)[2], int lane,
+                                             long long (&acc)[2], float (&sab)[2], int (&bad)[2]) {
     const int d = p.d;
     const uint16_t* xr = p.x + (size_t)t * d;
 #pragma unroll
-    for (int j = 0; j < EW; ++j) {
+    for (int j = 0; j < 2; ++j) {
         acc[j] = 0;
         sab[j] = 0.0f;
         bad[j] = 0;
     }
     for (int c0 = 0; c0 < d; c0 += 2048) {
-        uint4 xv[4], wv[EW][4];
+        uint4 xv[4], wv[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = c0 + lane * 8 + 512 * i;
             const bool ok = c < d;
             xv[i] = ok ? *(const uint4*)(xr + c) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < EW; ++j) {
-                const bool okj = ok && e0 + j < p.E;
-                wv[j][i] = okj ? *(const uint4*)(p.wr + (size_t)(e0 + j) * d + c) : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < 2; ++j) {
+                const bool okj = ok && ex[j] >= 0;
+                wv[j][i] = okj ? *(const uint4*)(p.wr + (size_t)ex[j] * d + c) : make_uint4(0, 0, 0, 0);
             }
         }
 #pragma unroll
-        for (int j = 0; j < EW; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 add_pair(xv[i].x, wv[j][i].x, acc[j], sab[j], bad[j]);
@@ -341,7 +340,7 @@ __device__ __forceinline__ void exact_logits(const RouteParams& p, int t, int e0
             }
     }
 #pragma unroll
-    for (int j = 0; j < EW; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             acc[j] += __shfl_xor(acc[j], off);
@@ -351,27 +350,97 @@ __device__ __forceinline__ void exact_logits(const RouteParams& p, int t, int e0
     }
 }
 
-// Routing and bucket sort in one launch of T * ceil(E / (4 * kRouteExpertsPerWave))
-// work-groups of 4 waves. Work-group (t, eb) computes the exact logits (int64,
-// units of 2^-48) of its experts for token t, kRouteExpertsPerWave per wave:
-// every product is an exponent-aligned integer mantissa product (add_pair), and
-// the sum is exact for any finite fp16 inputs with sum |x w| + |bias| < 2^15
-// (checked in fp32 with margin; outside it a status flag is raised). The
-// work-group that finishes token t last (a counter per
-// token) ranks all E exact logits (ties to the lower expert index), keeps the
-// top k and takes the softmax over them; the one that finishes the last token
-// does the bucket sort and the work lists. Values passed between work-groups
-// are device-coherent stores, drained before the counter increment that
-// publishes them, and device-coherent loads.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// fp32 logits of kRouteFilterPerWave experts e0, e0 + 1, ... for token t, one wave
+// (same column split as exact_logits): l = sum x w and s = sum |x w|, both with
+// v_dot2_f32_f16 (each product of two fp16 values is exact in fp32; only the
+// additions round). The bias is added by the caller.
+__device__ __forceinline__ void filter_logits(const RouteParams& p, int t, int e0, int lane,
+                                              float (&l)[kRouteFilterPerWave], float (&sa)[kRouteFilterPerWave]) {
+    constexpr int EF = kRouteFilterPerWave;
+    const int d = p.d;
+    const uint16_t* xr = p.x + (size_t)t * d;
+#pragma unroll
+    for (int j = 0; j < EF; ++j) l[j] = sa[j] = 0.0f;
+    for (int c0 = 0; c0 < d; c0 += 2048) {
+        uint4 xv[4], wv[EF][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + lane * 8 + 512 * i;
+            const bool ok = c < d;
+            xv[i] = ok ? *(const uint4*)(xr + c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < EF; ++j) {
+                const bool okj = ok && e0 + j < p.E;
+                wv[j][i] = okj ? *(const uint4*)(p.wr + (size_t)(e0 + j) * d + c) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < EF; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                const uint32_t ww[4] = {wv[j][i].x, wv[j][i].y, wv[j][i].z, wv[j][i].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    l[j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, xw[q]), __builtin_bit_cast(half2v, ww[q]),
+                                                  l[j], false);
+                    sa[j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, xw[q] & 0x7FFF7FFFu),
+                                                   __builtin_bit_cast(half2v, ww[q] & 0x7FFF7FFFu), sa[j], false);
+                }
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < EF; ++j) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            l[j] += __shfl_xor(l[j], off);
+            sa[j] += __shfl_xor(sa[j], off);
+        }
+    }
+}
+
+// Routing and bucket sort in one launch of T * ceil(E / (4 * kRouteFilterPerWave))
+// work-groups of 4 waves. The selection is exact (ties to the lower expert
+// index) without computing every logit exactly:
+//   1. work-group (t, eb) computes fp32 logits l_e (with the bias) and the sums
+//      s_e = sum |x w| + |bias| of its experts for token t. Every product is
+//      exact and at most d/32 + 32 rounded additions lie on the path of any
+//      term, so |l_e - L_e| <= err_e = (d/32 + 32) 2^-24 s_e (L_e the exact
+//      logit), inflated here by a margin for the rounding of s_e and of l_e -/+
+//      err_e themselves;
+//   2. the work-group that finishes token t last takes the k-th largest lower
+//      bound l_e - err_e; an expert whose upper bound l_e + err_e lies below it
+//      is beaten by k experts whatever the exact values, so only the others
+//      (candidates, usually k or a few more) get exact int64 logits in units of
+//      2^-48 (exponent-aligned integer mantissa products, add_pair), are ranked
+//      by exact key, and the top k get the softmax over their exact logits;
+//   3. the work-group that finishes the last token does the bucket sort and
+//      the work lists.
+// The sums are exact for finite fp16 inputs with sum |x w| + |bias| < 2^15
+// (checked in fp32 with margin for every expert; outside it, or for non-finite
+// inputs, a status flag is raised). Values passed between work-groups are
+// device-coherent stores, drained before the counter increment that publishes
+// them, and device-coherent loads.
+// For small T (exact_all) the first pass computes every logit exactly instead
+// (two experts per wave, spread over more work-groups), and every expert is a
+// candidate of the finisher: the exact work is then parallel rather than on
+// the finisher's path.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
-    constexpr int NW = kRouteThreads / 64, EW = kRouteExpertsPerWave;
+    constexpr int NW = kRouteThreads / 64, EF = kRouteFilterPerWave, EX = kRouteExactPerWave;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
-    const int nb = (E + NW * EW - 1) / (NW * EW);
+    const int per_wave = p.exact_all ? EX : EF;
+    const int nb = (E + NW * per_wave - 1) / (NW * per_wave);
     const int t = blockIdx.x / nb, eb = blockIdx.x - t * nb;
-    __shared__ long long s_ex[PW_MAX_EXPERTS + 8];   // + sentinels: the rank loop reads 8 at a time
+    __shared__ float s_lo[PW_MAX_EXPERTS];
+    __shared__ int s_cand[PW_MAX_EXPERTS + 8];   // candidate experts, + sentinels
+    __shared__ long long s_ex[PW_MAX_EXPERTS + 8];   // exact logits (of the candidates), + sentinels
     __shared__ long long s_selv[PW_MAX_TOP_K];
     __shared__ int s_sele[PW_MAX_TOP_K];
+    __shared__ int s_wcnt[NW];
+    __shared__ float s_kth;
     __shared__ int s_last;
     // bucket sort (last work-group only)
     __shared__ int s_cnt[PW_MAX_EXPERTS];
@@ -380,30 +449,50 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __shared__ int s_wc[NW * PW_MAX_EXPERTS];
     __shared__ int s_tmp[N_LISTS * NW];
 
-    // ---- exact logits of this work-group's experts; y = 0 for the token
+    // ---- 1. fp32 logits and bounds of this work-group's experts; y = 0 for the token
     if (eb == 0) {
         for (int c = tid; c < d; c += kRouteThreads) p.y[(size_t)t * d + c] = 0.0f;
     }
-    const int e0 = (eb * NW + wave) * EW;
-    if (e0 < E) {
-        long long acc[EW];
-        float sab[EW];
-        int bad[EW];
-        exact_logits(p, t, e0, lane, acc, sab, bad);
+    const int e0 = (eb * NW + wave) * per_wave;
+    if (p.exact_all) {
+        if (e0 < E) {
+            const int ex[2] = {e0, e0 + 1 < E ? e0 + 1 : -1};
+            long long acc[2];
+            float sab[2];
+            int bad[2];
+            exact_logits(p, t, ex, lane, acc, sab, bad);
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (ex[j] < 0) continue;
+                    if (p.bias) {
+                        const float bf = h2f(p.bias[ex[j]]);
+                        bad[j] |= !(fabsf(bf) < 32768.0f);
+                        if (!bad[j]) acc[j] += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
+                        sab[j] += fabsf(bf);
+                    }
+                    if (bad[j] || !(sab[j] < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
+                    store_agent(p.ws.lg + (size_t)t * E + ex[j], acc[j]);
+                }
+            }
+        }
+    } else if (e0 < E) {
+        float l[EF], sa[EF];
+        filter_logits(p, t, e0, lane, l, sa);
         if (lane == 0) {
 #pragma unroll
-            for (int j = 0; j < EW; ++j) {
+            for (int j = 0; j < EF; ++j) {
                 const int e = e0 + j;
                 if (e >= E) break;
                 if (p.bias) {
                     const float bf = h2f(p.bias[e]);
-                    bad[j] |= !(fabsf(bf) < 32768.0f);
-                    if (!bad[j]) acc[j] += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
-                    sab[j] += fabsf(bf);
+                    l[j] += bf;
+                    sa[j] += fabsf(bf);
                 }
-                // sum |x w| < 2^15 keeps every partial sum inside int64 (fp32 bound, wide margin)
-                if (bad[j] || !(sab[j] < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
-                store_agent(p.ws.lg + (size_t)t * E + e, acc[j]);
+                // outside the exact range (or non-finite): flagged, routing undefined
+                if (!(sa[j] < 32000.0f) || !(fabsf(l[j]) < 32768.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
+                const uint64_t pk = (uint64_t)__float_as_uint(l[j]) | ((uint64_t)__float_as_uint(sa[j]) << 32);
+                store_agent((unsigned long long*)(p.ws.lg + (size_t)t * E + e), (unsigned long long)pk);
             }
         }
     }
@@ -414,26 +503,115 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __syncthreads();
     if (!s_last) return;
 
-    // ---- token t: exact top-k by rank (number of experts ahead in key order)
-    if (tid == 0) store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
-    for (int i = tid; i < E; i += kRouteThreads) s_ex[i] = load_agent(p.ws.lg + (size_t)t * E + i);
-    // below every logit (|logit| < 2^63 by the range check): never ahead in key order
-    if (tid < 8) s_ex[E + tid] = LLONG_MIN;
-    __syncthreads();
-    if (tid < E) {
-        const long long v = s_ex[tid];
+    // ---- 2. token t: candidates by the fp32 bounds, then the exact top-k among them
+    if (tid == 0) {
+        store_agent(p.ws.tok_cnt + t, 0u);   // every work-group of the token has counted
+        s_kth = -INFINITY;                    // replaced below unless the bounds are not finite
+    }
+    if (tid < k) {   // valid expert ids whatever happens below (non-finite inputs are flagged)
+        s_sele[tid] = tid;
+        s_selv[tid] = LLONG_MIN;
+    }
+    // Rank of value v (expert e) among the n exact logits s_ex[0..n) of experts
+    // ids(c): the number ahead in key order; eight LDS reads in flight per step
+    // (entries n..n+7 are sentinels below every logit).
+    auto rank_of = [&](long long v, int e, int n, auto ids) {
         int rank = 0;
-        // eight LDS reads in flight per step instead of one dependent read per expert
-        for (int e0 = 0; e0 < E; e0 += 8) {
+        for (int c0 = 0; c0 < n; c0 += 8) {
             long long w[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = s_ex[e0 + j];
+            for (int j = 0; j < 8; ++j) w[j] = s_ex[c0 + j];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) rank += key_gt(w[j], e0 + j, v, tid) ? 1 : 0;
+            for (int j = 0; j < 8; ++j) rank += key_gt(w[j], ids(c0 + j), v, e) ? 1 : 0;
         }
-        if (rank < k) {
-            s_selv[rank] = v;
-            s_sele[rank] = tid;
+        return rank;
+    };
+    if (p.exact_all) {
+        // every logit already exact: rank all E experts
+        for (int i = tid; i < E; i += kRouteThreads) s_ex[i] = load_agent(p.ws.lg + (size_t)t * E + i);
+        if (tid < 8) s_ex[E + tid] = LLONG_MIN;   // below every logit (|logit| < 2^63 by the range check)
+        __syncthreads();
+        if (tid < E) {
+            const long long v = s_ex[tid];
+            const int rank = rank_of(v, tid, E, [](int c) { return c; });
+            if (rank < k) {
+                s_selv[rank] = v;
+                s_sele[rank] = tid;
+            }
+        }
+    } else {
+        const float g = (float)(d / 32 + 32) * 5.9604645e-8f * 1.01f;   // (d/32 + 32) * 2^-24, with margin
+        float lo = 0.0f, hi = 0.0f;
+        if (tid < E) {
+            const unsigned long long pk = load_agent((const unsigned long long*)(p.ws.lg + (size_t)t * E + tid));
+            const float l = __uint_as_float((uint32_t)pk), sa = __uint_as_float((uint32_t)(pk >> 32));
+            // the bound, widened so that the rounding of l -/+ err keeps it a bound
+            const float err = (g * sa + fabsf(l) * 2.4e-7f) * 1.0001f;
+            lo = l - err;
+            hi = l + err;
+            s_lo[tid] = lo;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int rank = 0;   // experts ahead of tid by lower bound (ties to the lower index)
+#pragma unroll 8
+            for (int e = 0; e < E; ++e) {
+                const float v = s_lo[e];
+                rank += (v > lo || (v == lo && e < tid)) ? 1 : 0;
+            }
+            if (rank == k - 1) s_kth = lo;
+        }
+        __syncthreads();
+        // candidates in increasing expert order (a non-finite bound makes every expert a candidate)
+        const bool cand = tid < E && !(hi < s_kth);
+        const unsigned long long bal = __ballot(cand);
+        if (lane == 0) s_wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, C = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            before += w < wave ? s_wcnt[w] : 0;
+            C += s_wcnt[w];
+        }
+        if (cand) s_cand[before + __popcll(bal & __lanemask_lt())] = tid;
+        if (tid < 8) {   // sentinels of the candidate ranking
+            s_ex[C + tid] = LLONG_MIN;
+            s_cand[C + tid] = PW_MAX_EXPERTS;
+        }
+        __syncthreads();
+        // exact logits of the candidates, two per wave and round
+        for (int c0 = 0; c0 < C; c0 += 2 * NW) {
+            const int ca = c0 + 2 * wave;
+            const int ex[2] = {ca < C ? s_cand[ca] : -1, ca + 1 < C ? s_cand[ca + 1] : -1};
+            long long acc[2];
+            float sab[2];
+            int bad[2];
+            exact_logits(p, t, ex, lane, acc, sab, bad);
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (ex[j] < 0) continue;
+                    if (p.bias) {
+                        const float bf = h2f(p.bias[ex[j]]);
+                        bad[j] |= !(fabsf(bf) < 32768.0f);
+                        if (!bad[j]) acc[j] += (long long)((double)bf * 281474976710656.0);  // * 2^48, exact
+                        sab[j] += fabsf(bf);
+                    }
+                    if (bad[j] || !(sab[j] < 32000.0f)) atomicOr(p.ws.status, PW_STATUS_ROUTER_RANGE);
+                    s_ex[ca + j] = acc[j];
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < C) {
+            const long long v = s_ex[tid];
+            const int e = s_cand[tid];
+            // candidates ahead in key order: larger exact logit, ties to the lower index
+            const int rank = rank_of(v, e, C, [&](int c) { return s_cand[c]; });
+            if (rank < k) {
+                s_selv[rank] = v;
+                s_sele[rank] = e;
+            }
         }
     }
     __syncthreads();
@@ -461,7 +639,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     __syncthreads();
     if (!s_last) return;
 
-    // ---- the last token: bucket sort and work lists for the expert kernel
+    // ---- 3. the last token: bucket sort and work lists for the expert kernel
     bucket_sort(p, s_cnt, s_off, s_run, s_wc, s_tmp);
 }
 
@@ -801,7 +979,8 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 // to the occupancy) the earliest unfinished item never waits: no deadlock. The
 // last work-group to finish zeroes the counters for the next launch.
 // NT: token tiles of 16 per item.
-template <int NT>
+// DET: deterministic accumulation (down items write their own partial rows).
+template <int NT, bool DET>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     // tid, r, kg are re-declared opaque at every item (below) so that the
@@ -1079,10 +1258,21 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                         const float wv = __int_as_float(tb[128 + tok_i]);
                         float* yr = g.y + (size_t)orow * g.d;
                         float* yo = yr + it.tile * 64 + row;   // set 0 rows; set 1 rows 32 further
-                        unsafeAtomicAdd(yo, wv * g0);
-                        unsafeAtomicAdd(yo + 1, wv * g1);
-                        unsafeAtomicAdd(yo + 32, wv * u0);
-                        unsafeAtomicAdd(yo + 33, wv * u1);
+                        if (DET) {
+                            // this (slot, K-piece)'s own row of the partial buffer: plain stores
+                            const int slot = tb[tok_i];
+                            const int prow = it.ex == g.E
+                                                 ? g.part_shared + (slot - g.shared_base) * p.dn.pieces_s + it.piece
+                                                 : slot * p.dn.pieces_r + it.piece;
+                            float* po = g.ws.part + (size_t)prow * g.d + it.tile * 64 + row;
+                            *(float2*)po = make_float2(wv * g0, wv * g1);
+                            *(float2*)(po + 32) = make_float2(wv * u0, wv * u1);
+                        } else {
+                            unsafeAtomicAdd(yo, wv * g0);
+                            unsafeAtomicAdd(yo + 1, wv * g1);
+                            unsafeAtomicAdd(yo + 32, wv * u0);
+                            unsafeAtomicAdd(yo + 33, wv * u1);
+                        }
                     }
                 }
             }
@@ -1154,6 +1344,7 @@ constexpr int kWStepBytes = 32 * 1024;
 
 __device__ __forceinline__ int w_frag(int s, int rh, int kh, int kg) { return ((s * 2 + rh) * 2 + kh) * 4 + kg; }
 
+template <bool DET>
 __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = kBigTokens / 16;   // token tiles per item (decode_item's group size)
@@ -1300,13 +1491,14 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
             int ntl = (it.nl - 64 * cw + 15) >> 4;
             ntl = ntl < 0 ? 0 : (ntl > 4 ? 4 : ntl);
             uint32_t boff[4];
-            int orow[4];
+            int orow[4], bslot[4];
             float wt[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int li = 64 * cw + 16 * t + tr;
                 boff[t] = kOOB;
                 orow[t] = -1;
+                bslot[t] = 0;
                 wt[t] = 0.0f;
                 if (li < it.nl) {
                     const int tkn = it.tbase + li;
@@ -1314,6 +1506,7 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
                     const int tok = sh ? tkn : g.ws.slot_tok[slotn];
                     const int brow = it.mode == 0 ? tok : slotn;
                     orow[t] = it.mode == 0 ? slotn : tok;
+                    bslot[t] = slotn;
                     wt[t] = (it.mode == 0 || sh) ? 1.0f : g.ws.slot_w[slotn];
                     boff[t] = (uint32_t)(brow * ldb + kq * 8);
                 }
@@ -1432,6 +1625,15 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
                                 // device-coherent store (written through), drained before the counter
                                 __hip_atomic_store((uint64_t*)(g.ws.act + (size_t)orow[t] * g.ld_act + it.tile * 32 + row),
                                                    v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            } else if (DET) {
+                                // this (slot, K-piece)'s own row of the partial buffer: plain stores
+                                const int prow = sh ? g.part_shared + (bslot[t] - g.shared_base) * p.dn.pieces_s + it.piece
+                                                    : bslot[t] * p.dn.pieces_r + it.piece;
+                                float* po = g.ws.part + (size_t)prow * g.d + it.tile * 64 + row;
+                                *(float4*)po = make_float4(wt[t] * acc[0][h][t][0], wt[t] * acc[0][h][t][1],
+                                                           wt[t] * acc[0][h][t][2], wt[t] * acc[0][h][t][3]);
+                                *(float4*)(po + 32) = make_float4(wt[t] * acc[1][h][t][0], wt[t] * acc[1][h][t][1],
+                                                                  wt[t] * acc[1][h][t][2], wt[t] * acc[1][h][t][3]);
                             } else {
                                 float* yo = g.y + (size_t)orow[t] * g.d + it.tile * 64 + row;
 #pragma unroll
@@ -1484,6 +1686,32 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint16_t* x, const 
                                                        uint16_t* out, long n) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i < n) out[i] = f2h(h2f(x[i]) + y[i]);
+}
+
+// Deterministic mode: each thread sums four columns of one token's partial rows in
+// a fixed order (routed assignments j = 0..k-1, each over its K-pieces, then
+// the shared expert's pieces), so y does not depend on the order in which the
+// down items ran.
+__global__ __launch_bounds__(256) void reduce_kernel(Workspace ws, float* y, int T, int k, int d, int pr, int ps,
+                                                     int part_shared) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;   // float4 index into y
+    const int q = d >> 2;
+    if (i >= (long)T * q) return;
+    const int t = (int)(i / q), c = (int)(i - (long)t * q) * 4;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto add = [&](int row) {
+        const float4 v = *(const float4*)(ws.part + (size_t)row * d + c);
+        a.x += v.x;
+        a.y += v.y;
+        a.z += v.z;
+        a.w += v.w;
+    };
+    for (int j = 0; j < k; ++j) {
+        const int slot = ws.slot_of[(size_t)t * k + j];
+        for (int pc = 0; pc < pr; ++pc) add(slot * pr + pc);
+    }
+    for (int pc = 0; pc < ps; ++pc) add(part_shared + t * ps + pc);
+    *(float4*)(y + (size_t)t * d + c) = a;
 }
 
 __global__ __launch_bounds__(64) void init_ws_kernel(Workspace ws, int n_counters, uint32_t wait_limit) {
@@ -1593,18 +1821,18 @@ hipError_t launch_init_ws(const Workspace& ws, int n_counters, uint32_t wait_lim
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-    constexpr int per_wg = (kRouteThreads / 64) * kRouteExpertsPerWave;
+    const int per_wg = (kRouteThreads / 64) * (p.exact_all ? kRouteExactPerWave : kRouteFilterPerWave);
     const int nb = (p.E + per_wg - 1) / per_wg;
     hipLaunchKernelGGL(route_kernel, dim3((unsigned)(p.T * nb)), dim3(kRouteThreads), 0, s, p);
     return hipGetLastError();
 }
 
-// Resident work-groups per CU of expert_kernel<NT> (0 if it cannot run).
-template <int NT>
+// Resident work-groups per CU of expert_kernel<NT, DET> (0 if it cannot run).
+template <int NT, bool DET>
 static hipError_t expert_occupancy(int* per_cu) {
     static int cached = -1;
     if (cached < 0) {
-        const void* f = (const void*)expert_kernel<NT>;
+        const void* f = (const void*)expert_kernel<NT, DET>;
         hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (err != hipSuccess) return err;
         int n = 0;
@@ -1628,30 +1856,31 @@ static bool cooperative_launch() {
     return on;
 }
 
-template <int NT>
+template <int NT, bool DET>
 static hipError_t launch_experts_t(const ExpertParams& p, int n_cu, hipStream_t s) {
     int per_cu = 0;
-    hipError_t err = expert_occupancy<NT>(&per_cu);
+    hipError_t err = expert_occupancy<NT, DET>(&per_cu);
     if (err != hipSuccess) return err;
     if (per_cu < 1) return hipErrorLaunchOutOfResources;
     // every work-group resident at once: the dependency waits rely on it
     if (cooperative_launch()) {
         ExpertParams arg = p;
         void* args[] = {(void*)&arg};
-        return hipLaunchCooperativeKernel((const void*)expert_kernel<NT>, dim3(per_cu * n_cu), dim3(256), args,
+        return hipLaunchCooperativeKernel((const void*)expert_kernel<NT, DET>, dim3(per_cu * n_cu), dim3(256), args,
                                           (unsigned)expert_lds_bytes(16 * NT), s);
     }
-    hipLaunchKernelGGL((expert_kernel<NT>), dim3(per_cu * n_cu), dim3(256), expert_lds_bytes(16 * NT), s, p);
+    hipLaunchKernelGGL((expert_kernel<NT, DET>), dim3(per_cu * n_cu), dim3(256), expert_lds_bytes(16 * NT), s, p);
     return hipGetLastError();
 }
 
 static int big_lds_bytes() { return kStripeBytes + 2 * kWStepBytes + 2 * kPreWords * 4 + 16; }   // + flag, ready
 
 // Resident work-groups per CU of the dequantise-once kernel (at most 1).
+template <bool DET>
 static hipError_t big_occupancy(int* per_cu) {
     static int cached = -1;
     if (cached < 0) {
-        const void* f = (const void*)expert_kernel_big;
+        const void* f = (const void*)expert_kernel_big<DET>;
         hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (err != hipSuccess) return err;
         int n = 0;
@@ -1663,32 +1892,48 @@ static hipError_t big_occupancy(int* per_cu) {
     return hipSuccess;
 }
 
-hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s) {
+template <bool DET>
+static hipError_t launch_big_t(const ExpertParams& p, int n_cu, hipStream_t s) {
     int per_cu = 0;
-    hipError_t err = big_occupancy(&per_cu);
+    hipError_t err = big_occupancy<DET>(&per_cu);
     if (err != hipSuccess) return err;
     if (per_cu < 1) return hipErrorLaunchOutOfResources;
     if (cooperative_launch()) {
         ExpertParams arg = p;
         void* args[] = {(void*)&arg};
-        return hipLaunchCooperativeKernel((const void*)expert_kernel_big, dim3(per_cu * n_cu), dim3(kBigWaves * 64),
-                                          args, (unsigned)big_lds_bytes(), s);
+        return hipLaunchCooperativeKernel((const void*)expert_kernel_big<DET>, dim3(per_cu * n_cu),
+                                          dim3(kBigWaves * 64), args, (unsigned)big_lds_bytes(), s);
     }
-    hipLaunchKernelGGL(expert_kernel_big, dim3(per_cu * n_cu), dim3(kBigWaves * 64), big_lds_bytes(), s, p);
+    hipLaunchKernelGGL(expert_kernel_big<DET>, dim3(per_cu * n_cu), dim3(kBigWaves * 64), big_lds_bytes(), s, p);
     return hipGetLastError();
 }
 
-hipError_t prepare_experts() {
-    int a = 0, b = 0, c = 0;
-    hipError_t err = expert_occupancy<1>(&a);
-    if (err == hipSuccess) err = expert_occupancy<4>(&b);
-    if (err == hipSuccess) err = big_occupancy(&c);
+hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s) {
+    return p.dn.det ? launch_big_t<true>(p, n_cu, s) : launch_big_t<false>(p, n_cu, s);
+}
+
+// Every expert-kernel variant the layer's flags can launch.
+hipError_t prepare_experts(bool det) {
+    int n[3] = {0, 0, 0};
+    hipError_t err = det ? expert_occupancy<1, true>(&n[0]) : expert_occupancy<1, false>(&n[0]);
+    if (err == hipSuccess) err = det ? expert_occupancy<4, true>(&n[1]) : expert_occupancy<4, false>(&n[1]);
+    if (err == hipSuccess) err = det ? big_occupancy<true>(&n[2]) : big_occupancy<false>(&n[2]);
     if (err != hipSuccess) return err;
-    return (a < 1 || b < 1 || c < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
+    return (n[0] < 1 || n[1] < 1 || n[2] < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
 }
 
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {
-    return tile_tokens == kSmallTokens ? launch_experts_t<1>(p, n_cu, s) : launch_experts_t<4>(p, n_cu, s);
+    if (p.dn.det)
+        return tile_tokens == kSmallTokens ? launch_experts_t<1, true>(p, n_cu, s) : launch_experts_t<4, true>(p, n_cu, s);
+    return tile_tokens == kSmallTokens ? launch_experts_t<1, false>(p, n_cu, s) : launch_experts_t<4, false>(p, n_cu, s);
+}
+
+hipError_t launch_reduce(const Workspace& ws, float* y, int T, int k, int d, int pr, int ps, int part_shared,
+                         hipStream_t s) {
+    const long n = (long)T * (d / 4);
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, y, T, k, d, pr, ps,
+                       part_shared);
+    return hipGetLastError();
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* x_next, long n,

@@ -21,15 +21,16 @@ class PagedMoELayer:
 
     def __init__(self, d_model: int, n_experts: int, d_ffn: int, top_k: int,
                  d_ffn_shared: int = 0, max_tokens: int = 256, lut_tiled: bool = False,
-                 rows_per_block: int = 0):
+                 rows_per_block: int = 0, deterministic: bool = False):
         self.d_model, self.n_experts, self.d_ffn = d_model, n_experts, d_ffn
         self.top_k, self.d_ffn_shared, self.max_tokens = top_k, d_ffn_shared, max_tokens
         self.n_total = n_experts + (1 if d_ffn_shared > 0 else 0)
         self.lut_tiled = lut_tiled
         self.rows_per_block = rows_per_block
+        self.deterministic = deterministic
+        flags = (B.PW_FLAG_LUT_TILED if lut_tiled else 0) | (B.PW_FLAG_DETERMINISTIC if deterministic else 0)
         self.handle = B.pw_layer_create(d_model, n_experts, d_ffn, top_k, d_ffn_shared, max_tokens,
-                                        flags=B.PW_FLAG_LUT_TILED if lut_tiled else 0,
-                                        rows_per_block=rows_per_block)
+                                        flags=flags, rows_per_block=rows_per_block)
         self._pages = {}
 
     def close(self):

@@ -94,8 +94,9 @@ typedef struct {
                               the shared expert has expert id E */
     int32_t max_tokens;    /* upper bound on T per forward, 1..65536, with
                               max_tokens*(top_k+1)*max(d_ffn, d_ffn_shared) < 2^31 */
-    uint32_t flags;        /* 0, or PW_FLAG_LUT_TILED: every bound LUT page of this layer
-                              is in the 32-row tiled order (default: row-major) */
+    uint32_t flags;        /* 0 or a combination of PW_FLAG_LUT_TILED (every bound LUT page
+                              of this layer is in the 32-row tiled order; default row-major)
+                              and PW_FLAG_DETERMINISTIC (see below) */
     int32_t rows_per_block;/* linear-block size: 0 = one block per linear; else a power of
                               two >= 64 dividing d_model, d_ffn and d_ffn_shared, and every
                               linear is cut into row-blocks of that many rows, each a
@@ -104,6 +105,16 @@ typedef struct {
 } pw_moe_desc;
 
 #define PW_FLAG_LUT_TILED 1u
+/* Deterministic accumulation: every forward of the same inputs gives the same y
+ * bit for bit. Each down-projection work item writes its weighted output rows to
+ * a partial buffer of its own (one fp32 row of d_model per routed assignment and
+ * K-piece of 2048 ffn columns, and per token and K-piece of the shared expert)
+ * instead of adding them into y with fp32 atomics, and a last kernel sums them per
+ * token in a fixed order (assignment j = 0..k-1, its pieces in order, then the
+ * shared expert's pieces). The layer's workspace grows by
+ * max_tokens * (top_k * ceil(d_ffn/2048) + ceil(d_ffn_shared/2048)) * d_model * 4
+ * bytes, and pw_moe_forward_noalloc's limit on T shrinks accordingly. */
+#define PW_FLAG_DETERMINISTIC 2u
 
 /* Optional routing outputs of a forward, all device pointers; any may be NULL.
  * topk_ids int32 [T][k] (descending logit, ties to the lower expert index),

@@ -44,10 +44,11 @@ def bind_all(layer, bits, pages):
         layer.bind(e, lin, [planes[p] for p in range(b)], luts[b], b)
 
 
-def gpu_layer(cfg, bits, pages, max_tokens=None, lut_tiled=False):
+def gpu_layer(cfg, bits, pages, max_tokens=None, lut_tiled=False, deterministic=False):
     from any_precision_bit_amd import PagedMoELayer
 
-    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, max_tokens or max(cfg.T, 1), lut_tiled=lut_tiled)
+    lay = PagedMoELayer(cfg.d, cfg.E, cfg.F, cfg.k, cfg.Fs, max_tokens or max(cfg.T, 1), lut_tiled=lut_tiled,
+                        deterministic=deterministic)
     lay.plan_set(bits)
     bind_all(lay, bits, pages)
     return lay

@@ -45,8 +45,9 @@ def test_create_validation(B):
     with pytest.raises(B.PwError) as ei:
         B.pw_layer_create(**ok, abi_version=99)
     assert ei.value.status == 1
-    B.pw_layer_destroy(B.pw_layer_create(**ok, flags=B.PW_FLAG_LUT_TILED))   # the one defined flag
-    for bad_flags in (2, 0x80000000):
+    for good in (B.PW_FLAG_LUT_TILED, B.PW_FLAG_DETERMINISTIC, B.PW_FLAG_LUT_TILED | B.PW_FLAG_DETERMINISTIC):
+        B.pw_layer_destroy(B.pw_layer_create(**ok, flags=good))   # the defined flags
+    for bad_flags in (4, 0x80000000):
         with pytest.raises(B.PwError) as ei:
             B.pw_layer_create(**ok, flags=bad_flags)
         assert ei.value.status == 1

@@ -172,6 +172,30 @@ def test_expert_paths(torch_dev, name, T):
         lay, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=lay, path=path, ref=ref)
 
 
+@pytest.mark.parametrize("name,T", [("qwen_d2048_t16", 300), ("mixtral_d4096", 64)])
+def test_deterministic_accumulation(torch_dev, name, T):
+    """PW_FLAG_DETERMINISTIC: two forwards of the same batch give bit-identical y on every expert
+    path, and each matches the oracle. qwen T = 300 runs the one-tile kernel (routed experts), the
+    dequantise-once kernel (the shared expert in two passes, three K-pieces); mixtral T = 64 runs
+    the one- and four-tile kernels with seven K-pieces per routed down projection."""
+    torch, dev = torch_dev
+    cfg = synth.CONFIGS[name].with_tokens(T)
+    _say(f"{name} T={T}: deterministic accumulation")
+    x, wr, bias = layer_inputs(cfg)
+    bits = synth.initial_bits(cfg)
+    blocks = _blocks(cfg, bits)
+    pages = device_pages(blocks, bits, dev)
+    lay = gpu_layer(cfg, bits, pages, max_tokens=T, deterministic=True)
+    subset = sample_tokens(T, 12, seed=5)
+    ref = None
+    for path in ["auto", "small", "four", "big"]:
+        lay, y, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=lay, path=path, ref=ref)
+        y2 = lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None if bias is None else to_dev_f16(bias, dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), path
+    lay.close()
+
+
 def _rewrite_all(cfg, layers, s):
     """The plan rewrite before step s (a multiple of the rewrite period): each layer's seeded blocks
     lose bits; the GPU layer is re-planned and the changed blocks rebound; the oracle follows."""
@@ -411,6 +435,28 @@ def test_ties_zero_input_and_determinism(torch_dev):
     assert rel_err_per_token(y2.cpu().numpy(), y.cpu().numpy()).max() <= 1e-5
 
 
+@pytest.mark.parametrize("T", [16, 48])
+def test_router_near_ties(torch_dev, T):
+    """Experts whose logits differ by one fp16 ulp of a single weight (times that column's x), and
+    an exact tie, at the top of every token; the oracle decides. At T = 16 the router computes
+    every logit exactly; at T = 48 its fp32 pass cannot order these experts, so the selection rests
+    on the exact logits of its candidates."""
+    cfg = synth.CONFIGS["tiny_d256"].with_tokens(T)
+    bits = synth.initial_bits(cfg)
+    blocks = _blocks(cfg, bits)
+    x, wr, _ = layer_inputs(cfg)
+    x = np.abs(x).astype(np.float16)
+    wr = wr.copy()
+    wr[1] = np.float16(0.02)
+    wr[2] = wr[1]
+    wr[2, 17] = np.nextafter(wr[1, 17], np.float16(1))      # one ulp up: expert 2 just ahead of 1
+    wr[3] = wr[1]
+    wr[3, 200] = np.nextafter(wr[1, 200], np.float16(0))    # one ulp down: expert 3 just behind 1
+    wr[4] = wr[1]                                           # exact tie with 1: the lower index wins
+    lay, y, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, None, np.arange(T, dtype=np.int32))
+    assert (ref["ids"] == np.array([2, 1])).all()           # (the construction: checked on the oracle)
+
+
 def test_plan_rewrite_and_rebind(torch_dev):
     torch, dev = torch_dev
     cfg = synth.CONFIGS["qwen_d2048_t16"].with_tokens(8)
@@ -429,11 +475,13 @@ def test_plan_rewrite_and_rebind(torch_dev):
                pages=pages)
 
 
-def test_router_range_flag(torch_dev):
+@pytest.mark.parametrize("T", [4, 48])
+def test_router_range_flag(torch_dev, T):
     """Outside the exact router's range (sum |x w| >= 2^15) or with a non-finite input the device
-    status word raises PW_STATUS_ROUTER_RANGE; reading it clears it."""
+    status word raises PW_STATUS_ROUTER_RANGE; reading it clears it (T = 4: every logit exact in
+    the first pass; T = 48: fp32 bounds first)."""
     torch, dev = torch_dev
-    cfg = synth.CONFIGS["tiny_d256"]
+    cfg = synth.CONFIGS["tiny_d256"].with_tokens(T)
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     lay = gpu_layer(cfg, bits, device_pages(blocks, bits, dev))
@@ -451,17 +499,19 @@ def test_router_range_flag(torch_dev):
         assert lay.status() == 0       # cleared by the read
 
 
-def test_router_full_fp16_range(torch_dev):
+@pytest.mark.parametrize("T", [16, 48])
+def test_router_full_fp16_range(torch_dev, T):
     """Exact routing for large but in-range inputs. Tokens 0..7 carry 16 columns with |x| in
-    [128, 4096], tokens 8..15 two columns with |x| in [128, 512]; router weights |w| in [128, 512] on
-    4 other columns of every third expert; sum |x w| stays far below 2^15. Routing (ids, weights,
-    counts, offsets, sorted order) must match the oracle's __int128 logits on every token with no
-    range flag. Outputs are compared on tokens 8..15: on tokens 0..7 the SwiGLU output exceeds
-    fp16's range, and the layer rounds it to fp16 as the down projection's MFMA operand."""
+    [128, 4096], the other tokens two columns with |x| in [128, 512]; router weights |w| in
+    [128, 512] on 4 other columns of every third expert; sum |x w| stays far below 2^15. Routing
+    (ids, weights, counts, offsets, sorted order) must match the oracle's __int128 logits on every
+    token with no range flag (T = 16: every logit exact in the first pass; T = 48: fp32 bounds,
+    then exact candidates). Outputs are compared on tokens 8 on: on tokens 0..7 the SwiGLU output
+    exceeds fp16's range, and the layer rounds it to fp16 as the down projection's MFMA operand."""
     torch, dev = torch_dev
     from any_precision_bit_amd import route_buffers
 
-    cfg = synth.CONFIGS["tiny_d256"].with_tokens(16)
+    cfg = synth.CONFIGS["tiny_d256"].with_tokens(T)
     bits = synth.initial_bits(cfg)
     blocks = _blocks(cfg, bits)
     x, wr, _ = layer_inputs(cfg)
@@ -470,23 +520,23 @@ def test_router_full_fp16_range(torch_dev):
     wr = wr.copy()
     sign = lambda shape: g.choice([-1.0, 1.0], size=shape)
     x[:8, :16] = (sign((8, 16)) * g.uniform(128, 4096, size=(8, 16))).astype(np.float16)
-    x[8:, 20:22] = (sign((8, 2)) * g.uniform(128, 512, size=(8, 2))).astype(np.float16)
+    x[8:, 20:22] = (sign((T - 8, 2)) * g.uniform(128, 512, size=(T - 8, 2))).astype(np.float16)
     wr[::3, 16:20] = (sign(wr[::3, 16:20].shape) * g.uniform(128, 512, size=wr[::3, 16:20].shape)).astype(np.float16)
     assert float((np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64)).T).max()) < 2 ** 15
     assert np.abs(x[:8].astype(np.float64)).max() > 2048
     _say("router full fp16 range")
     pages = device_pages(blocks, bits, dev)
-    lay = gpu_layer(cfg, bits, pages, max_tokens=16)
-    route = route_buffers(16, cfg.E, cfg.k, dev)
+    lay = gpu_layer(cfg, bits, pages, max_tokens=T)
+    route = route_buffers(T, cfg.E, cfg.k, dev)
     y = lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None, route=route)
     torch.cuda.synchronize()
     assert lay.status() == 0
-    sub = np.arange(8, 16, dtype=np.int32)
+    sub = np.arange(8, T, dtype=np.int32)
     ref = oracle.OracleLayer.from_config(cfg, bits, blocks).forward(x, wr, None, subset=sub)
     assert ref["status"] == 0
-    check_routing(route, ref, 16, cfg.E, cfg.k)
+    check_routing(route, ref, T, cfg.E, cfg.k)
     err = rel_err_per_token(y.cpu().numpy()[sub], ref["y"][sub])
-    _say(f"router full fp16 range: routing exact on 16 tokens, max rel err {err.max():.3e} on tokens 8..15")
+    _say(f"router full fp16 range: routing exact on {T} tokens, max rel err {err.max():.3e} on tokens 8..")
     assert err.max() <= REL_TOL
 
 
