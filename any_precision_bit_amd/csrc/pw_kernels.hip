@@ -965,8 +965,9 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 //   - act is written only with device-coherent (agent-scope, sc1) stores, which
 //     write through to memory; each producer wave drains them (vmcnt 0) before
 //     the work-group barrier after which thread 0 increments the counter;
-//   - the consumer polls the counter with device-coherent loads and issues no
-//     load of act (nor of any line holding act) before its wait ends, so no
+//   - the consumer (one wave polls, a barrier releases the others) reads the
+//     counter with device-coherent loads and issues no load of act (nor of any
+//     line holding act) before its wait ends, so no
 //     cache level can hold a stale copy of a piece's act lines: they were last
 //     touched by the previous launch, and a kernel boundary writes back and
 //     invalidates the non-coherent caches;
@@ -1086,17 +1087,23 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             const __amdgpu_buffer_rsrc_t brsrc =
                 it.mode == 0 ? make_rsrc(g.x, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
             if (it.mode == 1) {
-                // every gate_up item of this expert's K-piece has released its act rows
-                const uint32_t need = (uint32_t)((it.klen >> 5) * ((it.n_tok + 16 * NT - 1) / (16 * NT)));
-                const uint32_t* c = dep + it.pos * dstride + it.piece;
-                uint32_t polls = 0;
-                while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                    if (polls++ >= kconst(g.ws.wait_limit)[0]) {   // bounded: a missing producer becomes a flag
-                        if (tid == 0) atomicOr(g.ws.status, PW_STATUS_DEP_TIMEOUT);
-                        break;
+                // every gate_up item of this expert's K-piece has released its act rows:
+                // wave 0 polls the counter (one poller per work-group keeps the polls off
+                // the memory system) and the barrier releases the others; no wave loads
+                // act before it
+                if (q == 0) {
+                    const uint32_t need = (uint32_t)((it.klen >> 5) * ((it.n_tok + 16 * NT - 1) / (16 * NT)));
+                    const uint32_t* c = dep + it.pos * dstride + it.piece;
+                    uint32_t polls = 0;
+                    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+                        if (polls++ >= kconst(g.ws.wait_limit)[0]) {   // bounded: a missing producer becomes a flag
+                            if (tid == 0) atomicOr(g.ws.status, PW_STATUS_DEP_TIMEOUT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
                     }
-                    __builtin_amdgcn_s_sleep(1);
                 }
+                __syncthreads();
             }
             // the next item: its metadata and token rows now
             const int next = item + (int)gridDim.x;
