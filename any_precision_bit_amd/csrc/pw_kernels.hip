@@ -201,9 +201,22 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     constexpr int NW = kRouteThreads / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = p.E, n = p.T * p.k;
+    // ids and weights come from other work-groups through device-coherent loads, a
+    // memory round trip each: every loop below issues kSortBatch chunks' loads at once
+    constexpr int B = kSortBatch;
     for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kRouteThreads) atomicAdd(&s_cnt[load_agent(p.ws.ids + i)], 1);
+    for (int b0 = 0; b0 < n; b0 += B * kRouteThreads) {
+        int ev[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int i = b0 + u * kRouteThreads + tid;
+            ev[u] = i < n ? load_agent(p.ws.ids + i) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+            if (ev[u] >= 0) atomicAdd(&s_cnt[ev[u]], 1);
+    }
     __syncthreads();
     // exclusive offsets over experts (E <= kRouteThreads)
     {
@@ -227,12 +240,30 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     __syncthreads();
     // stable placement, kRouteThreads assignments at a time: lanes of one wave
     // with the same expert find each other by matching the 8 id bits
+    int ev[B];
+    float wv[B];
     for (int base = 0; base < n; base += kRouteThreads) {
+        const int u = (base / kRouteThreads) % B;   // this chunk's entry of the batch
+        if (u == 0) {
+#pragma unroll
+            for (int v = 0; v < B; ++v) {
+                const int i = base + v * kRouteThreads + tid;
+                ev[v] = i < n ? load_agent(p.ws.ids + i) : 0;
+                wv[v] = i < n ? load_agent(p.ws.w + i) : 0.0f;
+            }
+        }
         for (int j = tid; j < NW * E; j += kRouteThreads) s_wc[j] = 0;
         __syncthreads();
         const int i = base + tid;
         const bool valid = i < n;
-        const int e = valid ? load_agent(p.ws.ids + i) : 0;
+        int e = 0;
+        float wi = 0.0f;
+#pragma unroll
+        for (int v = 0; v < B; ++v)
+            if (v == u) {
+                e = ev[v];
+                wi = wv[v];
+            }
         unsigned long long same = __ballot(valid);
 #pragma unroll
         for (int bit = 0; bit < 8; ++bit) {
@@ -257,7 +288,7 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
             p.ws.sorted[pos] = i;
             p.ws.slot_of[i] = pos;
             p.ws.slot_tok[pos] = i / p.k;   // token of the slot, and its routing weight
-            p.ws.slot_w[pos] = load_agent(p.ws.w + i);
+            p.ws.slot_w[pos] = wi;
             if (p.o_sorted) p.o_sorted[pos] = i;
         }
         __syncthreads();
