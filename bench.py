@@ -763,6 +763,23 @@ def main():
         del cl2
         torch.cuda.empty_cache()
         log(f"mixtral_d4096 T=1: median {med:.1f} us")
+        # the headline layer with its LUT pages in the other accepted order (the 32-row tiled
+        # order is the kernel's preferred one; row-major is the per-row table of the pages)
+        other = "row-major" if args.lut_tiled else "tiled"
+        clt, *_ = make_clones(torch, synth, PagedMoELayer, dev, cfg, args.clones, lut_tiled=not args.lut_tiled)
+        ust = time_per_call(torch, clt, stream, max(args.steps, 50), args.warmup)
+        check_status([c["lay"] for c in clt], f"qwen_d2048_t16 ({other} LUT pages)")
+        medt = float(np.median(ust))
+        subs["qwen_d2048_t16_lut_" + other.replace("-", "_")] = {
+            "workload": synth.WORKLOAD_TEXT["qwen_d2048_t16"] + f", LUT pages {other}", "lut_pages": other,
+            "value": round(T / (medt * 1e-6), 1), "unit": "tokens/s", "us_median": round(medt, 2),
+            "us_p10": round(float(np.percentile(ust, 10)), 2), "us_p90": round(float(np.percentile(ust, 90)), 2),
+            "rotation_clones": args.clones, "calls": int(len(ust)), "status_checked": True}
+        for c in clt:
+            c["lay"].close()
+        del clt
+        torch.cuda.empty_cache()
+        log(f"qwen_d2048_t16 with {other} LUT pages: median {medt:.1f} us per forward")
         subs["qwen_stack24_t256"] = layer_stack(args, torch, synth, PagedMoELayer, lut_page, dev, print_table=False)
         log(f"qwen_stack24_t256: {subs['qwen_stack24_t256']['value']:,.0f} tokens/s")
         subs["page_movement"] = paging_run(args, torch, synth, PagedMoELayer, dev, print_table=False)
