@@ -6,12 +6,15 @@
 // and fuses routing, SwiGLU expert activation and weighted accumulation.
 //
 // Kernels, in stream order per forward:
-//   route_kernel   T * ceil(E/8) work-groups, two experts per wave: exact router
-//                  logits (int64, units of 2^-48); per token, the last work-group
-//                  takes the exact top-k and the softmax over the k selected; the
-//                  last token's work-group sorts the assignments by expert
-//                  (counts, offsets, stable order, each slot's token and weight)
-//                  and writes the per-expert work-item prefixes. Also y = 0.
+//   route_kernel   exact top-k routing: for T <= 32, T * ceil(E/4) work-groups
+//                  compute every exact router logit (int64, units of 2^-48, one
+//                  expert per wave); for larger T, T * ceil(E/16) work-groups
+//                  compute fp32 logits with error bounds and the finisher computes
+//                  exact logits of the candidates only. Per token, the last
+//                  work-group takes the exact top-k and the softmax over the k
+//                  selected; the last token's work-group sorts the assignments by
+//                  expert (counts, offsets, stable order, each slot's token and
+//                  weight) and writes the work lists. Also y = 0.
 //   expert_kernel  persistent, one launch per token-tile size: gate and up of
 //                  (expert, 32-row tile, token group) items (bit-plane unpack +
 //                  LUT dequant into MFMA A fragments, MFMA 16x16x32 fp16 with
@@ -19,6 +22,10 @@
 //                  64-row tile, K-piece, token group) items scaled by the
 //                  routing weight and atomically added into y; a down item waits
 //                  on a counter until its expert's act rows are complete.
+//   expert_kernel_big  experts with many tokens: producer waves dequantise each
+//                  weight once into LDS, consumer waves multiply it with up to 256
+//                  tokens.
+//   reduce_kernel  deterministic mode only: y from the down items' partial rows.
 //   residual_kernel  x_next = fp16_rne(x + y) when requested.
 //
 // Dequantisation (the hot loop). Lane (r, kg) of a wave owns row r (0..15) of
@@ -455,7 +462,7 @@ __device__ __forceinline__ void filter_logits(const RouteParams& p, int t, int e
 // device-coherent stores, drained before the counter increment that publishes
 // them, and device-coherent loads.
 // For small T (exact_all) the first pass computes every logit exactly instead
-// (two experts per wave, spread over more work-groups), and every expert is a
+// (one expert per wave, spread over more work-groups), and every expert is a
 // candidate of the finisher: the exact work is then parallel rather than on
 // the finisher's path.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
     const int e0 = (eb * NW + wave) * per_wave;
     if (p.exact_all) {
         if (e0 < E) {
-            const int ex[2] = {e0, e0 + 1 < E ? e0 + 1 : -1};
+            const int ex[2] = {e0, EX > 1 && e0 + 1 < E ? e0 + 1 : -1};
             long long acc[2];
             float sab[2];
             int bad[2];
