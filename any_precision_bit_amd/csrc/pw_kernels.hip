@@ -210,15 +210,20 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     const int E = p.E, n = p.T * p.k;
     // ids and weights come from other work-groups through device-coherent loads, a
     // memory round trip each: every loop below issues kSortBatch chunks' loads at once
+    // (when every assignment fits one batch, T*k <= kSortBatch*kRouteThreads, the
+    // counting pass also loads the weights and the placement reuses both)
     constexpr int B = kSortBatch;
+    const bool one_batch = n <= B * kRouteThreads;
+    int ev[B];
+    float wv[B];
     for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
     __syncthreads();
     for (int b0 = 0; b0 < n; b0 += B * kRouteThreads) {
-        int ev[B];
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int i = b0 + u * kRouteThreads + tid;
             ev[u] = i < n ? load_agent(p.ws.ids + i) : -1;
+            wv[u] = i < n && one_batch ? load_agent(p.ws.w + i) : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < B; ++u)
@@ -247,11 +252,9 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
     __syncthreads();
     // stable placement, kRouteThreads assignments at a time: lanes of one wave
     // with the same expert find each other by matching the 8 id bits
-    int ev[B];
-    float wv[B];
     for (int base = 0; base < n; base += kRouteThreads) {
         const int u = (base / kRouteThreads) % B;   // this chunk's entry of the batch
-        if (u == 0) {
+        if (u == 0 && !one_batch) {
 #pragma unroll
             for (int v = 0; v < B; ++v) {
                 const int i = base + v * kRouteThreads + tid;
