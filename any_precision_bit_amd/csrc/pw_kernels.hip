@@ -468,7 +468,9 @@ __device__ __forceinline__ void filter_logits(const RouteParams& p, int t, int e
 // (one expert per wave, spread over more work-groups), and every expert is a
 // candidate of the finisher: the exact work is then parallel rather than on
 // the finisher's path.
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
+// Four waves per SIMD (at most 128 VGPRs, no spills): four work-groups per CU
+// keep more first-pass and finisher work in flight at large T.
+__global__ __launch_bounds__(kRouteThreads) __attribute__((amdgpu_waves_per_eu(4))) void route_kernel(RouteParams p) {
     constexpr int NW = kRouteThreads / 64, EF = kRouteFilterPerWave, EX = kRouteExactPerWave;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = p.d, E = p.E, k = p.k;
@@ -620,10 +622,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
             s_cand[C + tid] = PW_MAX_EXPERTS;
         }
         __syncthreads();
-        // exact logits of the candidates, two per wave and round
-        for (int c0 = 0; c0 < C; c0 += 2 * NW) {
-            const int ca = c0 + 2 * wave;
-            const int ex[2] = {ca < C ? s_cand[ca] : -1, ca + 1 < C ? s_cand[ca + 1] : -1};
+        // exact logits of the candidates, one per wave and round (two per wave
+        // would hold both rows' loads and sums live: 231 VGPRs instead of 106)
+        for (int c0 = 0; c0 < C; c0 += NW) {
+            const int ca = c0 + wave;
+            const int ex[2] = {ca < C ? s_cand[ca] : -1, -1};
             long long acc[2];
             float sab[2];
             int bad[2];
