@@ -1043,6 +1043,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
     uint32_t* const dep = g.ws.dep;
     const int dstride = g.ws.dep_stride;
     const int npos = g.E + g.has_shared;
+    // A work-group without an item leaves at once and takes no part in the
+    // finished-work-group count (a launch whose lists are empty costs little).
+    const int n_all = g.ws.prefix[p.gu.list * (g.E + 2) + npos] + g.ws.prefix[p.dn.list * (g.E + 2) + npos];
+    if ((int)blockIdx.x >= n_all) return;
+    const uint32_t n_working = (uint32_t)min((int)gridDim.x, n_all);
     // Work-group w takes items w, w + G, w + 2G, ... of the combined order (G =
     // grid size): no shared counter, and the next item is always known.
     for (int i = tid; i <= npos; i += 256) {
@@ -1347,7 +1352,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
         vm_drain();   // this work-group's counter increments (thread 0's) are performed
         const uint32_t prev = __hip_atomic_fetch_add(dep + (size_t)npos * dstride, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = prev == gridDim.x - 1u;
+        *s_flag = prev == n_working - 1u;
     }
     __syncthreads();
     if (*s_flag) {
@@ -1410,6 +1415,10 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
     uint32_t* const dep = g.ws.dep;
     const int dstride = g.ws.dep_stride;
     const int npos = g.E + g.has_shared;
+    // a work-group without an item leaves at once (as in expert_kernel)
+    const int n_all = g.ws.prefix[p.gu.list * (g.E + 2) + npos] + g.ws.prefix[p.dn.list * (g.E + 2) + npos];
+    if ((int)blockIdx.x >= n_all) return;
+    const uint32_t n_working = (uint32_t)min((int)gridDim.x, n_all);
     for (int i = tid; i <= npos; i += kBigWaves * 64) {
         s_pre[i] = g.ws.prefix[p.gu.list * (g.E + 2) + i];
         s_pre[kPreWords + i] = g.ws.prefix[p.dn.list * (g.E + 2) + i];
@@ -1722,7 +1731,7 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
         vm_drain();
         const uint32_t prev = __hip_atomic_fetch_add(dep + (size_t)npos * dstride, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = prev == gridDim.x - 1u;
+        *s_flag = prev == n_working - 1u;
     }
     __syncthreads();
     if (*s_flag) {
