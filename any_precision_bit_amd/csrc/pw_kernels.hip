@@ -798,6 +798,21 @@ __device__ __forceinline__ void lut_stage_load(LutStage& st, const uint16_t* lut
     }
 }
 
+// The same loads as buffer loads whose instruction count never depends on b or on
+// `valid` (units past 2^b, and every unit when !valid, read zeros without touching
+// memory), so that a wait issued after them can be counted exactly.
+__device__ __forceinline__ void lut_stage_load_buf(LutStage& st, const uint16_t* lut0, int b0,
+                                                   const uint16_t* lut1, int b1, int tid, int tiled, bool valid) {
+    const __amdgpu_buffer_rsrc_t r0 = make_rsrc(lut0, valid ? (64u << b0) : 0u);
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(lut1, valid ? (64u << b1) : 0u);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int u = tid + it * 256;
+        st.v[0][it] = buf_load16(r0, u < (4 << b0) ? lut_unit_offset(u, b0, tiled) * 2u : kOOB);
+        st.v[1][it] = buf_load16(r1, u < (4 << b1) ? lut_unit_offset(u, b1, tiled) * 2u : kOOB);
+    }
+}
+
 // Debug-kernel stripe (dword idx*64 + row, both halves the same) from the LUTs
 // of 32 rows (row-major, or 32-row tiled), one wave, plain loop.
 __device__ __forceinline__ void stage_lut32(uint32_t* stripe, const uint16_t* tile, int b, int tiled, int lane) {
@@ -860,6 +875,27 @@ __device__ __forceinline__ TokInfo fetch_tokinfo(const GemmParams& p, const Item
             tk.w = sh ? 1.0f : p.ws.slot_w[slot];
         }
     }
+    return tk;
+}
+
+// fetch_tokinfo for either list with a fixed instruction count: the slot's token
+// and weight are buffer loads (zeros for the shared expert, for threads past the
+// group and when !valid), the list's mode picks the fields afterwards.
+__device__ __forceinline__ TokInfo fetch_tokinfo_buf(const GemmParams& p, const Item& it, int tid, bool valid) {
+    constexpr uint32_t kAny = 0x7FFFFFF0u;   // records: lanes that must not load use kOOB
+    const bool sh = it.ex == p.E;
+    const int base = kconst(p.ws.offsets)[it.ex];   // offsets has E + 1 entries
+    const int tkn = it.tbase + tid;
+    const bool in = valid && tid < it.nl;
+    const int slot = sh ? (p.shared_base + tkn) : (base + tkn);
+    const uint32_t off = (in && !sh) ? (uint32_t)slot * 4u : kOOB;
+    const int tokv = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.ws.slot_tok, kAny), (int)off, 0, 0));
+    const float wv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.ws.slot_w, kAny), (int)off, 0, 0));
+    const int tok = sh ? tkn : tokv;
+    TokInfo tk;
+    tk.brow = it.mode == 0 ? tok : slot;
+    tk.orow = it.mode == 0 ? slot : tok;
+    tk.w = it.mode == 0 ? 0.0f : (sh ? 1.0f : wv);
     return tk;
 }
 
@@ -1075,10 +1111,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
         // first column of this lane's 128 columns in chunk ch (relative to the item's K range)
         auto lane_col = [&](int ch) { return ch * 1024 + kh * 512 + kg * 128; };
         // plane loads of chunk ch (line ch of the item's K range) into (c0, c1):
-        // slot i holds plane i - (8 - b); absent planes and columns past the range read zeros
-        auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8]) {
+        // slot i holds plane i - (8 - b); absent planes and columns past the range read zeros.
+        // Group grp (0..3) is slots 7 - 2 grp and 6 - 2 grp of both sets (the present planes
+        // of a small b come first); grp < 0 loads all of them.
+        auto load_chunk = [&](const Item& it, int ch, uint4 (&c0)[8], uint4 (&c1)[8], int grp = -1,
+                              bool valid = true) {
             const int Kb = it.K >> 3;
-            const bool vg = lane_col(ch) < it.klen;
+            const bool vg = valid && lane_col(ch) < it.klen;
             const uint32_t nrec = (uint32_t)(it.R * Kb);
             const int cb = (it.kbase + lane_col(ch)) >> 3;
             const int row = rh * 16 + r;
@@ -1086,7 +1125,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
             const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 7; i >= 0; --i) {
+                if (grp >= 0 && (7 - i) / 2 != grp) continue;
                 c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
                 c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
             }
@@ -1198,12 +1238,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             // complete in issue order, so a fragment loaded after a prefetch is
             // waited on only together with it.
             half8 bfr[NT][4];
-            auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8]) {
-                if (ch * 1024 + kh * 512 >= it.klen) return;
+            // pf(dw) issues group dw of the prefetch into the other plane buffer right
+            // after dword dw's B fragments: a wait for those fragments then covers only
+            // the groups issued a dword or more before, not the whole next chunk.
+            auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8], auto pf) {
+                const bool active = ch * 1024 + kh * 512 < it.klen;   // wave-uniform
                 const bool vg = lane_col(ch) < it.klen;
 #pragma unroll
                 for (int dw = 0; dw < 4; ++dw) {
-                    if (dw > 0) load_b(ch, dw, bfr, vg);
+                    if (dw > 0 && active) load_b(ch, dw, bfr, vg);
+                    pf(dw);
+                    if (!active) continue;
                     uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -1234,11 +1279,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             bool fetched = false;
             // The next item's planes, LUT rows and token rows only: never its B rows,
             // which for a down item may only be read after its dependency wait.
-            auto fetch_next = [&]() {
+            auto fetch_next = [&]() {   // all at once, after the item's last chunk
                 if (has_next) {
                     load_chunk(nit, 0, pa0, pa1);
                     lut_load(nit, st);
-                    ntk = tokinfo(nit);   // its scalar loads are waited together with the chunk's
+                    ntk = tokinfo(nit);
                 }
                 fetched = true;
             };
@@ -1246,17 +1291,31 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 if (ch < nch) load_b(ch, 0, bfr, lane_col(ch) < it.klen);
             };
             first_b(0);
-            if (1 < nch) load_chunk(it, 1, pb0, pb1);
+            // Chunk ch computes from one plane buffer while the other receives the next
+            // chunk, or the next item's first chunk (which always goes to pa), one
+            // group per dword of ch. Every group issues its loads whether or not there
+            // is anything to fetch (then they read zeros), so the waits stay exact;
+            // the next item's LUT and token rows follow the last group.
 #pragma unroll 1
             for (int ch = 0; ch < nch; ch += 2) {
-                compute_chunk(ch, pa0, pa1);
+                compute_chunk(ch, pa0, pa1, [&](int dw) {
+                    load_chunk(it, ch + 1, pb0, pb1, dw, ch + 1 < nch);
+                });
                 first_b(ch + 1);
-                if (ch + 2 < nch) load_chunk(it, ch + 2, pa0, pa1);
-                else if (ch + 1 < nch) fetch_next();
                 if (ch + 1 >= nch) break;
-                compute_chunk(ch + 1, pb0, pb1);
+                const bool nx = ch + 2 >= nch;   // the next item's first chunk
+                compute_chunk(ch + 1, pb0, pb1, [&](int dw) {
+                    load_chunk(nx ? nit : it, nx ? 0 : ch + 2, pa0, pa1, dw, !nx || has_next);
+                    if (dw == 3) {
+                        const int b0 = nit.blk0->bits, b1 = nit.blk1->bits;
+                        lut_stage_load_buf(st, (const uint16_t*)nit.blk0->lut + ((size_t)nit.rows0 << b0), b0,
+                                           (const uint16_t*)nit.blk1->lut + ((size_t)nit.rows1 << b1), b1, tid,
+                                           g.lut_tiled, nx && has_next);
+                        ntk = fetch_tokinfo_buf(nit.mode == 0 ? p.gu : p.dn, nit, tid, nx && has_next);
+                    }
+                });
+                if (nx) fetched = true;
                 first_b(ch + 2);
-                if (ch + 3 < nch) load_chunk(it, ch + 3, pb0, pb1);
             }
             if (!fetched) fetch_next();
 
