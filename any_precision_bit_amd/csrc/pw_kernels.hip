@@ -737,6 +737,33 @@ __device__ __forceinline__ half8 lut_fragment(const uint32_t (&rw)[8], int m, ui
     return a;
 }
 
+// The A fragments of step m of both row-sets (set 0: low halves of the stripe
+// dwords, set 1: high halves), with all 16 lookups issued before the first value
+// is packed: the scheduler otherwise waits on each batch of eight, exposing the
+// LDS latency at two waves per SIMD.
+__device__ __forceinline__ void lut_fragments2(const uint32_t (&rw0)[8], const uint32_t (&rw1)[8], int m,
+                                               uint32_t slot, half8& a0, half8& a1) {
+    uint32_t ad0[8], ad1[8];
+    _Float16 v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ad0[j] = __builtin_amdgcn_perm(rw0[j], slot, 0x03020400u | (uint32_t)(m << 8));
+        ad1[j] = __builtin_amdgcn_perm(rw1[j], slot, 0x03020400u | (uint32_t)(m << 8)) + 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v0[j] = *(lds_half*)(size_t)ad0[j];
+        v1[j] = *(lds_half*)(size_t)ad1[j];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // scheduling group: the 16 LDS reads,
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // then VALU
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a0[j] = v0[j];
+        a1[j] = v1[j];
+    }
+}
+
 // 8 LUT entries [c8, c8+8) of one row as four packed fp16 pairs (zeros past 2^b).
 // A row of b < 3 is 4 or 8 bytes; it is read whole (c8 is 0 then).
 __device__ __forceinline__ uint4 load_lut8(const uint16_t* row, int b, int c8) {
@@ -1259,8 +1286,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     slots_to_indices(w1, rw1);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const half8 a0 = lut_fragment(rw0, m, slot, 0);
-                        const half8 a1 = lut_fragment(rw1, m, slot, 2);
+                        half8 a0, a1;
+                        lut_fragments2(rw0, rw1, m, slot, a0, a1);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             if (NT == 1 || nt < ntl) {   // a one-tile item always holds a token
