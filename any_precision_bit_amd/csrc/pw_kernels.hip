@@ -1185,15 +1185,23 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
         __syncthreads();
         int par = 0;
         // The two work-groups sharing a CU (w and w + G/2 in dispatch order)
-        // compete for its SIMDs, and at equal priority the older waves win, so
-        // the later work-group runs its items ~25 % slower. Their wave
-        // priorities swap every item so that both progress at the same rate.
-        const int slot = blockIdx.x >= gridDim.x / 2 ? 1 : 0;
+        // compete for its SIMDs, and at equal priority the older waves win: the
+        // later work-group runs its items ~25 % slower. When their item counts
+        // are within that ratio, their wave priorities swap every item so that
+        // both progress at the same rate; when one has at least 5/4 of the
+        // other's items (say 4 against 3), it keeps the higher priority.
+        const int half = (int)gridDim.x / 2;
+        const int slot = (int)blockIdx.x >= half ? 1 : 0;
+        const int partner = slot ? (int)blockIdx.x - half : (int)blockIdx.x + half;
+        auto items_of = [&](int w) { return w < (int)gridDim.x && w < n_items ? (n_items - 1 - w) / (int)gridDim.x + 1 : 0; };
+        const int mine = items_of((int)blockIdx.x), theirs = items_of(partner);
+        const int prio_mode = 4 * mine >= 5 * theirs ? 1 : 4 * theirs >= 5 * mine ? 2 : 0;   // 1 high, 2 low, 0 swap
         int round = 0;
 
         while (true) {
             asm volatile("" : "+v"(tid), "+v"(r), "+v"(kg));
-            if (((round++ ^ slot) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+            const bool high = prio_mode == 0 ? ((round++ ^ slot) & 1) != 0 : prio_mode == 1;
+            if (high) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
             const int nch = n_chunks(it);
             const int ntl = (it.nl + 15) >> 4;
