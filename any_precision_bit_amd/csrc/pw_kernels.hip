@@ -1150,12 +1150,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             const int row = rh * 16 + r;
             const uint32_t off0 = vg ? (uint32_t)((it.rows0 + row) * Kb + cb) : kOOB;
             const uint32_t off1 = vg ? (uint32_t)((it.rows1 + row) * Kb + cb) : kOOB;
-            const int s0 = 8 - it.blk0->bits, s1 = 8 - it.blk1->bits;
+            // the page-table entries are re-read (scalar cache) at every group rather
+            // than kept: descriptors of two items' 16 planes do not fit the scalar
+            // registers and would be spilled to vector-register lanes
+            auto bk0 = it.blk0, bk1 = it.blk1;
+            asm volatile("" : "+s"(bk0), "+s"(bk1));
+            const int s0 = 8 - bk0->bits, s1 = 8 - bk1->bits;
 #pragma unroll
             for (int i = 7; i >= 0; --i) {
                 if (grp >= 0 && (7 - i) / 2 != grp) continue;
-                c0[i] = buf_load16(make_rsrc((const void*)it.blk0->planes[i], i >= s0 ? nrec : 0u), off0);
-                c1[i] = buf_load16(make_rsrc((const void*)it.blk1->planes[i], i >= s1 ? nrec : 0u), off1);
+                c0[i] = buf_load16(make_rsrc((const void*)bk0->planes[i], i >= s0 ? nrec : 0u), off0);
+                c1[i] = buf_load16(make_rsrc((const void*)bk1->planes[i], i >= s1 ? nrec : 0u), off1);
             }
         };
         auto n_chunks = [](const Item& it) { return (it.klen + 1023) >> 10; };
