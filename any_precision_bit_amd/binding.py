@@ -194,7 +194,7 @@ def pw_debug_set_wait_limit(layer: int, polls: int) -> None:
     _check(lib.pw_debug_set_wait_limit(layer, polls))
 
 
-PATHS = {"auto": 0, "small": 1, "four": 2, "big": 3}
+PATHS = {"auto": 0, "small": 1, "four": 2, "big": 3, "two": 4}
 
 
 def pw_debug_set_path(layer: int, path) -> None:

@@ -25,7 +25,7 @@
 #include "pw_internal.h"
 
 static_assert(PW_PATH_AUTO == pw::PATH_AUTO && PW_PATH_SMALL == pw::PATH_SMALL && PW_PATH_FOUR == pw::PATH_FOUR &&
-                  PW_PATH_BIG == pw::PATH_BIG,
+                  PW_PATH_BIG == pw::PATH_BIG && PW_PATH_TWO == pw::PATH_TWO,
               "path values of the ABI and of the launcher");
 
 using pw::DevBlock;
@@ -351,6 +351,7 @@ int default_path() {
         if (!strcmp(v, "small")) return (int)pw::PATH_SMALL;
         if (!strcmp(v, "four")) return (int)pw::PATH_FOUR;
         if (!strcmp(v, "big")) return (int)pw::PATH_BIG;
+        if (!strcmp(v, "two")) return (int)pw::PATH_TWO;
         return (int)pw::PATH_AUTO;
     }();
     return path;
@@ -372,9 +373,16 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     r.path = path;
     pw::RouteParams& rp = r.rp;
     rp.exact_all = T <= pw::kRouteExactAllMax ? 1 : 0;
-    rp.small_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0 : pw::kSmallMax;
-    rp.four_max = path == pw::PATH_SMALL ? INT_MAX : path == pw::PATH_BIG ? 0
-                : path == pw::PATH_FOUR ? INT_MAX : (T >= pw::kBigBatch ? pw::kFourMaxBig : pw::kFourMax);
+    // the small lists' token group: 32 when the routed experts average more than
+    // one 16-token tile (T k > 16 E), so that an expert of 17..32 tokens is one
+    // item per tile (each weight dequantised once) in the two-tile kernel; below
+    // that most experts fit one tile, and the one-tile kernel's double-buffered
+    // planes run them faster (measured: mixtral_d4096 T = 64, fine_e128 T = 128)
+    rp.small_tokens = path == pw::PATH_SMALL ? pw::kSmallTokens : path == pw::PATH_TWO ? pw::kTwoTokens
+                    : ((long)T * k > (long)pw::kSmallTokens * E ? pw::kTwoTokens : pw::kSmallTokens);
+    rp.small_max = (path == pw::PATH_SMALL || path == pw::PATH_TWO) ? INT_MAX : path == pw::PATH_BIG ? 0 : pw::kSmallMax;
+    rp.four_max = (path == pw::PATH_SMALL || path == pw::PATH_TWO || path == pw::PATH_FOUR) ? INT_MAX
+                : path == pw::PATH_BIG ? 0 : (T >= pw::kBigBatch ? pw::kFourMaxBig : pw::kFourMax);
     rp.x = (const uint16_t*)x;
     rp.wr = (const uint16_t*)router_w;
     rp.bias = (const uint16_t*)router_b;
@@ -449,7 +457,7 @@ pw_status launch_phase(const pw_launch& r, int d_model, int phase, hipStream_t s
             ep.gu.list = pw::LIST_GU_SMALL;
             ep.dn.list = pw::LIST_DN_SMALL;
             // a kernel is launched when some expert can reach its token range
-            if (r.rp.small_max > 0 && (e = pw::launch_experts(pw::kSmallTokens, ep, r.n_cu, s)) != hipSuccess)
+            if (r.rp.small_max > 0 && (e = pw::launch_experts(r.rp.small_tokens, ep, r.n_cu, s)) != hipSuccess)
                 return hip_fail(e, "expert kernel");
             if (T > r.rp.small_max && r.rp.four_max > r.rp.small_max) {
                 ep.gu.list = pw::LIST_GU_FOUR;
@@ -865,7 +873,7 @@ pw_status pw_debug_dequant(const void* const* planes, int32_t b, const void* lut
 pw_status pw_debug_set_path(pw_layer L, int32_t path) {
     g_err.clear();
     if (!L) return fail(PW_E_ARG, "pw_debug_set_path: null layer");
-    if (path < PW_PATH_AUTO || path > PW_PATH_BIG) return fail(PW_E_ARG, "path %d not in 0..3", path);
+    if (path < PW_PATH_AUTO || path > PW_PATH_TWO) return fail(PW_E_ARG, "path %d not in 0..4", path);
     L->path = path;
     return PW_OK;
 }

@@ -67,7 +67,8 @@ struct RouteParams {
     float* y;              // zeroed here
     int exact_all;         // 1: exact logits of every expert in the first pass (small T); 0: fp32
                            // bounds first, exact logits of the candidates only
-    int small_max;         // experts with 1..small_max tokens: one-tile lists (16-token groups)
+    int small_tokens;      // token group of the small lists: 16 (one-tile kernel) or 32 (two-tile)
+    int small_max;         // experts with 1..small_max tokens: small lists
     int four_max;          // small_max+1..four_max tokens: four-tile lists (64-token groups);
                            // more: dequantise-once lists (256-token groups)
     int32_t* o_ids;        // optional caller copies of the routing outputs
@@ -134,7 +135,8 @@ int plan_greedy(const PlanProblem& P, double bytes_to_free, uint8_t* bits, doubl
 
 hipError_t launch_init_ws(const Workspace& ws, int n_counters, uint32_t wait_limit, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
-// tile_tokens: kSmallTokens (one MFMA token tile per item) or kLargeTokens (four).
+// tile_tokens: kSmallTokens (one MFMA token tile per item), kTwoTokens (two) or
+// kLargeTokens (four).
 // The grid is every work-group the device can hold at once (per-CU occupancy x n_cu).
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s);
 // The dequantise-once kernel over the large lists (groups of kBigTokens tokens).
@@ -161,7 +163,9 @@ hipError_t scratch_memory(int dev, void** ptr, size_t* bytes);
 int expert_lds_bytes(int tile_tokens);
 
 constexpr int kSmallTokens = 16;          // token group of the one-tile kernel (one 16-token MFMA tile)
-constexpr int kSmallMax = 32;             // experts with 1..32 tokens: groups of 16 in the one-tile kernel
+constexpr int kTwoTokens = 32;            // token group of the two-tile kernel
+constexpr int kSmallMax = 32;             // experts with 1..32 tokens: the small lists, in groups of 16,
+                                          // or of 32 when T k > 16 E (each weight dequantised once)
 constexpr int kLargeTokens = 64;          // four-tile kernel: groups of 64 tokens
 constexpr int kBigTokens = 256;           // dequantise-once kernel: groups of 256 tokens
 // Experts with 33..kFourMax tokens go to the four-tile kernel (one or two
@@ -173,12 +177,14 @@ constexpr int kFourMax = 128;
 constexpr int kFourMaxBig = 64;
 constexpr int kBigBatch = 512;
 // Which kernel takes which experts (PW_FORCE_PATH, pw_debug_set_path):
-//   AUTO  1..kSmallMax tokens: one-tile kernel; up to kFourMax (kFourMaxBig when
-//         T >= kBigBatch): four-tile kernel; more: dequantise-once kernel
+//   AUTO  1..kSmallMax tokens: two-tile kernel when T k > 16 E, else one-tile kernel;
+//         up to kFourMax (kFourMaxBig when T >= kBigBatch): four-tile kernel;
+//         more: dequantise-once kernel
 //   SMALL every expert in the one-tile kernel (16-token groups)
-//   FOUR  1..kSmallMax: one-tile kernel; more: four-tile kernel (64-token groups)
+//   FOUR  1..kSmallMax: as AUTO; more: four-tile kernel (64-token groups)
 //   BIG   every expert in the dequantise-once kernel
-enum { PATH_AUTO = 0, PATH_SMALL = 1, PATH_FOUR = 2, PATH_BIG = 3 };
+//   TWO   every expert in the two-tile kernel (32-token groups)
+enum { PATH_AUTO = 0, PATH_SMALL = 1, PATH_FOUR = 2, PATH_BIG = 3, PATH_TWO = 4 };
 constexpr int kDownPiece = 2048;          // K columns of one down item (partial sums add into y)
 // act rows of one K-piece start on a 128-byte line (2-byte elements): a line never holds two pieces
 static_assert(kDownPiece % 64 == 0, "K-pieces must start on 128-byte act lines");

@@ -319,12 +319,12 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
             tgu = sh ? p.tiles_gu_s : p.tiles_gu_r;
             pdn = sh ? p.pieces_dn_s : p.pieces_dn_r;
         }
-        // up to small_max tokens: 16-token groups in the one-tile kernel (at two
-        // work-groups per CU, two such items cost less CU time than one item of
-        // a large kernel at one work-group per CU); up to four_max: 64-token
-        // groups in the four-tile kernel; beyond: 256-token groups in the
-        // dequantise-once kernel
-        const int small = (cnt >= 1 && cnt <= p.small_max) ? (cnt + kSmallTokens - 1) / kSmallTokens : 0;
+        // up to small_max tokens: groups of small_tokens (16 or 32) in the one- or
+        // two-tile kernel (two work-groups per CU: two such items cost less CU time
+        // than one item of a large kernel at one work-group per CU); up to
+        // four_max: 64-token groups in the four-tile kernel; beyond: 256-token
+        // groups in the dequantise-once kernel
+        const int small = (cnt >= 1 && cnt <= p.small_max) ? (cnt + p.small_tokens - 1) / p.small_tokens : 0;
         const int four = (cnt > p.small_max && cnt <= p.four_max) ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
         const int big = cnt > p.four_max ? (cnt + kBigTokens - 1) / kBigTokens : 0;
         const int tdn = p.tiles_dn * pdn;
@@ -1086,10 +1086,15 @@ __device__ __forceinline__ void lut_stage_write(unsigned char* stripe, const Lut
 // increasing order, so with all work-groups resident (the launch sizes the grid
 // to the occupancy) the earliest unfinished item never waits: no deadlock. The
 // last work-group to finish zeroes the counters for the next launch.
-// NT: token tiles of 16 per item.
+// NT: token tiles of 16 per item. NT = 1 and 2 run two work-groups per CU,
+// NT = 4 one. NT = 2 keeps a single plane buffer (the registers of the second
+// one hold its second token tile's accumulators and B fragments): the next
+// chunk's planes load right after the current chunk's last transposes, and
+// the lookups and MFMAs of its last 32 columns cover their latency.
 // DET: deterministic accumulation (down items write their own partial rows).
 template <int NT, bool DET>
-__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertParams p) {
+__global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void expert_kernel(ExpertParams p) {
+    constexpr bool SB = NT == 2;   // single plane buffer
     extern __shared__ __align__(16) unsigned char smem[];
     // tid, r, kg are re-declared opaque at every item (below) so that the
     // compiler recomputes values derived from them instead of keeping dozens of
@@ -1281,14 +1286,19 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
             // pf(dw) issues group dw of the prefetch into the other plane buffer right
             // after dword dw's B fragments: a wait for those fragments then covers only
             // the groups issued a dword or more before, not the whole next chunk.
+            // With a single plane buffer (SB), pf(dw) is called after dword dw's
+            // transposes, when the buffer's words have been read.
             auto compute_chunk = [&](int ch, const uint4 (&c0)[8], const uint4 (&c1)[8], auto pf) {
                 const bool active = ch * 1024 + kh * 512 < it.klen;   // wave-uniform
                 const bool vg = lane_col(ch) < it.klen;
 #pragma unroll
                 for (int dw = 0; dw < 4; ++dw) {
                     if (dw > 0 && active) load_b(ch, dw, bfr, vg);
-                    pf(dw);
-                    if (!active) continue;
+                    if (!SB) pf(dw);
+                    if (!active) {
+                        if (SB) pf(dw);
+                        continue;
+                    }
                     uint32_t w0[8], w1[8], rw0[8], rw1[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -1297,13 +1307,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                     }
                     slots_to_indices(w0, rw0);
                     slots_to_indices(w1, rw1);
+                    if (SB) pf(dw);
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         half8 a0, a1;
                         lut_fragments2(rw0, rw1, m, slot, a0, a1);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
-                            if (NT == 1 || nt < ntl) {   // a one-tile item always holds a token
+                            // unguarded up to two tiles (a one-tile item always holds a
+                            // token; an empty second tile multiplies zero B fragments), so
+                            // each step stays one basic block the scheduler can interleave
+                            if (NT <= 2 || nt < ntl) {
                                 acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[nt][m], acc0[nt], 0, 0, 0);
                                 acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[nt][m], acc1[nt], 0, 0, 0);
                             }
@@ -1331,13 +1345,32 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void expert_kernel(ExpertPara
                 if (ch < nch) load_b(ch, 0, bfr, lane_col(ch) < it.klen);
             };
             first_b(0);
+            if constexpr (SB) {
+                // one buffer: after the last transposes of chunk ch it receives chunk
+                // ch + 1, or the next item's first chunk (loads issued whether or not
+                // there is anything to fetch); the next item's LUT and token rows load
+                // after the last MFMAs, once the B fragments' registers are free
+#pragma unroll 1
+                for (int ch = 0; ch < nch; ++ch) {
+                    const bool nx = ch + 1 >= nch;
+                    compute_chunk(ch, pa0, pa1, [&](int dw) {
+                        if (dw == 3) load_chunk(nx ? nit : it, nx ? 0 : ch + 1, pa0, pa1, -1, !nx || has_next);
+                    });
+                    first_b(ch + 1);
+                }
+                if (has_next) {
+                    lut_load(nit, st);
+                    ntk = tokinfo(nit);
+                }
+                fetched = true;
+            }
             // Chunk ch computes from one plane buffer while the other receives the next
             // chunk, or the next item's first chunk (which always goes to pa), one
             // group per dword of ch. Every group issues its loads whether or not there
             // is anything to fetch (then they read zeros), so the waits stay exact;
             // the next item's LUT and token rows follow the last group.
 #pragma unroll 1
-            for (int ch = 0; ch < nch; ch += 2) {
+            for (int ch = 0; ch < (SB ? 0 : nch); ch += 2) {
                 compute_chunk(ch, pa0, pa1, [&](int dw) {
                     load_chunk(it, ch + 1, pb0, pb1, dw, ch + 1 < nch);
                 });
@@ -1997,7 +2030,7 @@ static hipError_t expert_occupancy(int* per_cu) {
         int n = 0;
         err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, expert_lds_bytes(16 * NT));
         if (err != hipSuccess) return err;
-        cached = n < (NT == 1 ? 2 : 1) ? n : (NT == 1 ? 2 : 1);
+        cached = n < (NT <= 2 ? 2 : 1) ? n : (NT <= 2 ? 2 : 1);
     }
     *per_cu = cached;
     return hipSuccess;
@@ -2073,18 +2106,24 @@ hipError_t launch_experts_big(const ExpertParams& p, int n_cu, hipStream_t s) {
 
 // Every expert-kernel variant the layer's flags can launch.
 hipError_t prepare_experts(bool det) {
-    int n[3] = {0, 0, 0};
+    int n[4] = {0, 0, 0, 0};
     hipError_t err = det ? expert_occupancy<1, true>(&n[0]) : expert_occupancy<1, false>(&n[0]);
-    if (err == hipSuccess) err = det ? expert_occupancy<4, true>(&n[1]) : expert_occupancy<4, false>(&n[1]);
-    if (err == hipSuccess) err = det ? big_occupancy<true>(&n[2]) : big_occupancy<false>(&n[2]);
+    if (err == hipSuccess) err = det ? expert_occupancy<2, true>(&n[1]) : expert_occupancy<2, false>(&n[1]);
+    if (err == hipSuccess) err = det ? expert_occupancy<4, true>(&n[2]) : expert_occupancy<4, false>(&n[2]);
+    if (err == hipSuccess) err = det ? big_occupancy<true>(&n[3]) : big_occupancy<false>(&n[3]);
     if (err != hipSuccess) return err;
-    return (n[0] < 1 || n[1] < 1 || n[2] < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
+    return (n[0] < 1 || n[1] < 1 || n[2] < 1 || n[3] < 1) ? hipErrorLaunchOutOfResources : hipSuccess;
+}
+
+template <bool DET>
+static hipError_t launch_experts_d(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {
+    if (tile_tokens == kSmallTokens) return launch_experts_t<1, DET>(p, n_cu, s);
+    if (tile_tokens == kTwoTokens) return launch_experts_t<2, DET>(p, n_cu, s);
+    return launch_experts_t<4, DET>(p, n_cu, s);
 }
 
 hipError_t launch_experts(int tile_tokens, const ExpertParams& p, int n_cu, hipStream_t s) {
-    if (p.dn.det)
-        return tile_tokens == kSmallTokens ? launch_experts_t<1, true>(p, n_cu, s) : launch_experts_t<4, true>(p, n_cu, s);
-    return tile_tokens == kSmallTokens ? launch_experts_t<1, false>(p, n_cu, s) : launch_experts_t<4, false>(p, n_cu, s);
+    return p.dn.det ? launch_experts_d<true>(tile_tokens, p, n_cu, s) : launch_experts_d<false>(tile_tokens, p, n_cu, s);
 }
 
 hipError_t launch_reduce(const Workspace& ws, float* y, int T, int k, int d, int pr, int ps, int part_shared,

@@ -300,21 +300,25 @@ pw_status pw_debug_set_wait_limit(pw_layer layer, uint32_t polls);
 
 /* A/B switch: which expert kernel takes which experts in later forwards of
  * this layer (same results up to fp32 summation order):
- *   PW_PATH_AUTO  experts with 1..32 tokens: the one-tile kernel (16-token
+ *   PW_PATH_AUTO  experts with 1..32 tokens: the two-tile kernel (one 32-token
+ *                 group) when the T*top_k assignments exceed 16 per routed
+ *                 expert on average, else the one-tile kernel (16-token
  *                 groups); 33..128 (33..64 when T >= 512): the four-tile
  *                 kernel (64-token groups); more: the dequantise-once kernel
  *                 (256-token groups)
- *   PW_PATH_SMALL every expert in the one-tile kernel
- *   PW_PATH_FOUR  1..32 tokens: one-tile kernel; more: the four-tile kernel
+ *   PW_PATH_SMALL every expert in the one-tile kernel (16-token groups)
+ *   PW_PATH_FOUR  as PW_PATH_AUTO up to 32 tokens; more: the four-tile kernel
  *                 (64-token groups, every weight dequantised once per group)
  *   PW_PATH_BIG   every expert in the dequantise-once kernel
+ *   PW_PATH_TWO   every expert in the two-tile kernel (32-token groups)
  * New layers start from the environment variable PW_FORCE_PATH (auto, small,
- * four or big; read once per process), else PW_PATH_AUTO. PW_E_ARG for a null
- * layer or another value. */
+ * four, big or two; read once per process), else PW_PATH_AUTO. PW_E_ARG for a
+ * null layer or another value. */
 #define PW_PATH_AUTO 0
 #define PW_PATH_SMALL 1
 #define PW_PATH_FOUR 2
 #define PW_PATH_BIG 3
+#define PW_PATH_TWO 4
 pw_status pw_debug_set_path(pw_layer layer, int32_t path);
 
 #ifdef __cplusplus

@@ -148,10 +148,10 @@ def test_fine_e128(torch_dev):
 @pytest.mark.parametrize("name,T", [("tiny_d256", 200), ("fine_e128_t128", 128), ("qwen_d2048_t16", 300)])
 def test_expert_paths(torch_dev, name, T):
     """Every A/B path of the expert kernels on the same layer and batch: the one-tile kernel alone,
-    the four-tile kernel for experts above 32 tokens, the dequantise-once kernel for them (the
-    default) and for every expert. T = 300 puts the qwen shared expert in two 256-token passes
-    (a ragged 44-token second pass); tiny_d256 and fine_e128_t128 have routed experts above 32
-    tokens."""
+    the two-tile kernel alone (32-token groups, ragged last groups), the four-tile kernel for
+    experts above 32 tokens, the dequantise-once kernel for them (the default) and for every
+    expert. T = 300 puts the qwen shared expert in two 256-token passes (a ragged 44-token second
+    pass); tiny_d256 and fine_e128_t128 have routed experts above 32 tokens."""
     cfg = synth.CONFIGS[name].with_tokens(T)
     _say(f"{name} T={T}: expert paths")
     x, wr, bias = layer_inputs(cfg)
@@ -168,16 +168,17 @@ def test_expert_paths(torch_dev, name, T):
         subset = np.unique(np.concatenate([toks[:12], np.arange(0, T, 23), [T - 1]])).astype(np.int32)
     assert counts.max() > 32 or (cfg.Fs > 0 and T > 256)
     lay, ref = None, None
-    for path in ["auto", "small", "four", "big"]:
+    for path in ["auto", "small", "two", "four", "big"]:
         lay, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=lay, path=path, ref=ref)
 
 
 @pytest.mark.parametrize("name,T", [("qwen_d2048_t16", 300), ("mixtral_d4096", 64)])
 def test_deterministic_accumulation(torch_dev, name, T):
     """PW_FLAG_DETERMINISTIC: two forwards of the same batch give bit-identical y on every expert
-    path, and each matches the oracle. qwen T = 300 runs the one-tile kernel (routed experts), the
-    dequantise-once kernel (the shared expert in two passes, three K-pieces); mixtral T = 64 runs
-    the one- and four-tile kernels with seven K-pieces per routed down projection."""
+    path, and each matches the oracle. qwen T = 300 runs the two-tile kernel (routed experts, T k
+    above 16 per expert) and the dequantise-once kernel (the shared expert in two passes, three
+    K-pieces); mixtral T = 64 runs the one- and four-tile kernels with seven K-pieces per routed
+    down projection; the two path runs both layers in the two-tile kernel."""
     torch, dev = torch_dev
     cfg = synth.CONFIGS[name].with_tokens(T)
     _say(f"{name} T={T}: deterministic accumulation")
@@ -188,7 +189,7 @@ def test_deterministic_accumulation(torch_dev, name, T):
     lay = gpu_layer(cfg, bits, pages, max_tokens=T, deterministic=True)
     subset = sample_tokens(T, 12, seed=5)
     ref = None
-    for path in ["auto", "small", "four", "big"]:
+    for path in ["auto", "small", "two", "four", "big"]:
         lay, y, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, subset, layer=lay, path=path, ref=ref)
         y2 = lay.forward(to_dev_f16(x, dev), to_dev_f16(wr, dev), None if bias is None else to_dev_f16(bias, dev))
         torch.cuda.synchronize()
@@ -386,13 +387,17 @@ TWO_GROUPS = synth.MoEConfig("gtwo", 93, d=256, E=4, F=384, k=2, T=32, Fs=512,
 
 
 def test_two_token_groups_one_kernel(torch_dev):
-    """T = 32: experts with 17..32 tokens (and the 32-token shared expert) run as two
-    16-token groups in the one-tile kernel; no 64-token launch."""
+    """T = 32: experts with 17..32 tokens (and the 32-token shared expert) run as two 16-token
+    groups in the one-tile kernel (the default at this T k / E) and as one 32-token group in the
+    two-tile kernel (the two path); no 64-token launch."""
     cfg = TWO_GROUPS
     bits = synth.initial_bits(cfg)
     blocks = synth.make_layer_blocks(cfg, bits)
     x, wr, bias = layer_inputs(cfg)
-    _, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32))
+    lay, ref = None, None
+    for path in ["auto", "two"]:
+        lay, _, ref = run_parity(torch_dev, cfg, bits, blocks, x, wr, bias, np.arange(cfg.T, dtype=np.int32),
+                                 layer=lay, path=path, ref=ref)
     assert ((ref["counts"] > 16) & (ref["counts"] <= 32)).any(), ref["counts"]
 
 
