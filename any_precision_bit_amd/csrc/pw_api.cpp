@@ -372,7 +372,7 @@ pw_launch make_launch(const pw_layer_s* L, const void* x, int T, const void* rou
     r.n_cu = n_cu;
     r.path = path;
     pw::RouteParams& rp = r.rp;
-    rp.exact_all = T <= pw::kRouteExactAllMax ? 1 : 0;
+    rp.exact_all = (long)T * E <= pw::kRouteExactAllWork ? 1 : 0;
     // the small lists' token group: 32 when the routed experts average more than
     // one 16-token tile (T k > 16 E), so that an expert of 17..32 tokens is one
     // item per tile (each weight dequantised once) in the two-tile kernel; below

@@ -191,7 +191,9 @@ static_assert(kDownPiece % 64 == 0, "K-pieces must start on 128-byte act lines")
 constexpr int kRouteThreads = 256;          // route kernel: 4 waves
 constexpr int kRouteFilterPerWave = 4;      // router rows per wave in the fp32 pass
 constexpr int kRouteExactPerWave = 1;       // router rows per wave when every logit is exact
-constexpr int kRouteExactAllMax = 32;       // T up to which every logit is computed exactly
+constexpr int kRouteExactAllWork = 2048;    // T * E up to which every logit is computed exactly in the
+                                            // first pass (its T * E / 4 work-groups are all resident at
+                                            // once); above it, fp32 bounds and exact candidates
 constexpr int kSortBatch = 8;               // bucket sort: chunks of assignments loaded per round trip
 constexpr int kMaxModel = 8192;           // d_model limit (x row staged in LDS)
 

@@ -6,9 +6,9 @@
 // and fuses routing, SwiGLU expert activation and weighted accumulation.
 //
 // Kernels, in stream order per forward:
-//   route_kernel   exact top-k routing: for T <= 32, T * ceil(E/4) work-groups
+//   route_kernel   exact top-k routing: for T * E <= 2048, T * ceil(E/4) work-groups
 //                  compute every exact router logit (int64, units of 2^-48, one
-//                  expert per wave); for larger T, T * ceil(E/16) work-groups
+//                  expert per wave); for more, T * ceil(E/16) work-groups
 //                  compute fp32 logits with error bounds and the finisher computes
 //                  exact logits of the candidates only. Per token, the last
 //                  work-group takes the exact top-k and the softmax over the k
@@ -464,7 +464,7 @@ __device__ __forceinline__ void filter_logits(const RouteParams& p, int t, int e
 // inputs, a status flag is raised). Values passed between work-groups are
 // device-coherent stores, drained before the counter increment that publishes
 // them, and device-coherent loads.
-// For small T (exact_all) the first pass computes every logit exactly instead
+// For small T * E (exact_all) the first pass computes every logit exactly instead
 // (one expert per wave, spread over more work-groups), and every expert is a
 // candidate of the finisher: the exact work is then parallel rather than on
 // the finisher's path.
