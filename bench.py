@@ -37,6 +37,7 @@ def log(*a):
 
 KERNEL_SRC = os.path.join(ROOT, "any_precision_bit_amd", "csrc", "pw_kernels.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_kernel_qwen_d2048_t16_traffic.md")
+SQ_PROFILE = os.path.join(ROOT, "profiles", "expert_kernel_qwen_d2048_t16_sq_counters.md")
 
 
 def kernel_code_digest():
@@ -46,18 +47,32 @@ def kernel_code_digest():
     return hashlib.sha256("\n".join(c for c in code if c).encode()).hexdigest()
 
 
+def profile_values(path, keys):
+    """The "key: value" lines of a committed rocprofv3 counter summary, as floats, or None when
+    the file is missing or the kernel code has changed since those counters were taken."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(tuple(k + ":" for k in keys)))
+    if fields.get("kernel_code_sha256", "").strip() != kernel_code_digest():
+        return None
+    return {k: float(fields[k]) for k in keys if k != "kernel_code_sha256" and k in fields}
+
+
 def measured_traffic():
     """HBM bytes per expert-kernel launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE runs, scaled by a 1 GiB copy's readings), or None
     when the kernel code has changed since those counters were taken."""
-    try:
-        text = open(TRAFFIC_PROFILE).read()
-    except OSError:
-        return None
-    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("kernel_code_sha256:", "traffic_bytes_per_launch:")))
-    if fields.get("kernel_code_sha256", "").strip() != kernel_code_digest():
-        return None
-    return float(fields["traffic_bytes_per_launch"])
+    v = profile_values(TRAFFIC_PROFILE, ["kernel_code_sha256", "traffic_bytes_per_launch"])
+    return None if not v else v["traffic_bytes_per_launch"]
+
+
+def measured_alu():
+    """The expert kernel's VALU and LDS lane-instructions per dequantised weight and its
+    VALU-issue time from the committed SQ counter summary (None if the kernel changed)."""
+    return profile_values(SQ_PROFILE, ["kernel_code_sha256", "valu_lane_instr_per_weight",
+                                       "lds_lane_instr_per_weight", "valu_bound_us"])
 
 
 # (label, workload, tokens or None for the workload's own, rotation clones); tiny_d256 is cache-resident
@@ -733,7 +748,8 @@ def main():
     roofline = {"bound": "hbm", "kernel": "expert_kernel<1> (gate_up + SwiGLU + down + accumulation)",
                 "achieved": round(ex_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ex_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "bytes_per_launch": phase_bytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3)}
+                "bytes_per_launch": phase_bytes[1], "avg_launch_us": round(avg_ms[1] * 1e3, 3),
+                "alu": measured_alu()}
     for c in clones:
         c["lay"].close()
     del clones
