@@ -70,7 +70,7 @@ struct RouteParams {
     int small_tokens;      // token group of the small lists: 16 (one-tile kernel) or 32 (two-tile)
     int small_max;         // experts with 1..small_max tokens: small lists
     int four_max;          // small_max+1..four_max tokens: four-tile lists (64-token groups);
-                           // more: dequantise-once lists (256-token groups)
+                           // more: dequantise-once lists (128-token groups)
     int32_t* o_ids;        // optional caller copies of the routing outputs
     float* o_w;
     int32_t* o_counts;
@@ -167,7 +167,7 @@ constexpr int kTwoTokens = 32;            // token group of the two-tile kernel
 constexpr int kSmallMax = 32;             // experts with 1..32 tokens: the small lists, in groups of 16,
                                           // or of 32 when T k > 16 E (each weight dequantised once)
 constexpr int kLargeTokens = 64;          // four-tile kernel: groups of 64 tokens
-constexpr int kBigTokens = 256;           // dequantise-once kernel: groups of 256 tokens
+constexpr int kBigTokens = 128;           // dequantise-once kernel: groups of 128 tokens
 // Experts with 33..kFourMax tokens go to the four-tile kernel (one or two
 // 64-token groups). The dequantise-once kernel has the higher cost per item and
 // pays off once a forward brings it many items: from kBigBatch tokens on, the

@@ -322,7 +322,7 @@ __device__ void bucket_sort(const RouteParams& p, int* s_cnt, int* s_off, int* s
         // up to small_max tokens: groups of small_tokens (16 or 32) in the one- or
         // two-tile kernel (two work-groups per CU: two such items cost less CU time
         // than one item of a large kernel at one work-group per CU); up to
-        // four_max: 64-token groups in the four-tile kernel; beyond: 256-token
+        // four_max: 64-token groups in the four-tile kernel; beyond: 128-token
         // groups in the dequantise-once kernel
         const int small = (cnt >= 1 && cnt <= p.small_max) ? (cnt + p.small_tokens - 1) / p.small_tokens : 0;
         const int four = (cnt > p.small_max && cnt <= p.four_max) ? (cnt + kLargeTokens - 1) / kLargeTokens : 0;
@@ -1503,7 +1503,7 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void expert_kernel(ExpertPara
 //
 // Work-group of 8 waves, one per CU. Items are those of the large lists, with
 // the same rows and K ranges as in expert_kernel (gate_up: 32 rows of gate and
-// of up; down: 64 rows, one K-piece) and up to 256 tokens each.
+// of up; down: 64 rows, one K-piece) and up to kBigTokens = 128 tokens each.
 //   - Waves 0..3 (producers) unpack and look up exactly as expert_kernel does
 //     (wave q: rows 16*(q >> 1) .. +15, half-line q & 1; lane (r, kg)), but
 //     write the looked-up weights to LDS instead of multiplying them. One step
@@ -1512,11 +1512,11 @@ __global__ __launch_bounds__(256, NT <= 2 ? 2 : 1) void expert_kernel(ExpertPara
 //     columns are contiguous: fragment (set, row half, kh, kg) holds columns
 //     kh*512 + kg*128 + 32*dw + [0, 32) of the chunk, lane (r, kq) of it the
 //     eight columns 8*kq .. +7 (the producer's lookup step m = kq).
-//   - Waves 4..7 (consumers) take 64 tokens each (four 16-token MFMA tiles)
+//   - Waves 4..7 (consumers) take 32 tokens each (two 16-token MFMA tiles)
 //     and multiply every fragment of a step with their tokens' activation
 //     fragments (x rows or act rows, loaded straight from L2: per token 64
 //     contiguous bytes per fragment, 16 rows per load instruction),
-//     accumulating the whole item (64 rows x 64 tokens) in registers; the
+//     accumulating the whole item (64 rows x 32 tokens) in registers; the
 //     epilogue is expert_kernel's (SwiGLU -> act, or w * o added into y).
 // Steps are pipelined through two 32 KiB buffers: in phase f the producers
 // write step f into buffer f & 1 while the consumers read step f - 1 from the
@@ -1663,7 +1663,8 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
         }
     } else if (wave >= 4 && (int)blockIdx.x < n_items) {
         // ------------------------------------------------------------ consumers
-        const int cw = wave - 4;              // tokens 64*cw .. +63 of the item
+        constexpr int TPW = kBigTokens / 64;  // 16-token tiles per consumer wave
+        const int cw = wave - 4;              // tokens 16*TPW*cw .. +16*TPW-1 of the item
         const int tr = lane & 15, kq = lane >> 4;
         int item = blockIdx.x;
         Item it = decode(item);
@@ -1677,17 +1678,17 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
             const int ldb = it.mode == 0 ? g.d : g.ld_act;
             const __amdgpu_buffer_rsrc_t brsrc =
                 it.mode == 0 ? make_rsrc(g.x, p.gu.b_bytes) : make_rsrc(g.ws.act, p.dn.b_bytes);
-            // this wave's tokens: B row, output row and weight of token 64*cw + 16*t + tr
+            // this wave's tokens: B row, output row and weight of token 16*TPW*cw + 16*t + tr
             const bool sh = it.ex == g.E;
             const int obase = sh ? 0 : kconst(g.ws.offsets)[it.ex];
-            int ntl = (it.nl - 64 * cw + 15) >> 4;
-            ntl = ntl < 0 ? 0 : (ntl > 4 ? 4 : ntl);
-            uint32_t boff[4];
-            int orow[4], bslot[4];
-            float wt[4];
+            int ntl = (it.nl - 16 * TPW * cw + 15) >> 4;
+            ntl = ntl < 0 ? 0 : (ntl > TPW ? TPW : ntl);
+            uint32_t boff[TPW];
+            int orow[TPW], bslot[TPW];
+            float wt[TPW];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int li = 64 * cw + 16 * t + tr;
+            for (int t = 0; t < TPW; ++t) {
+                const int li = 16 * TPW * cw + 16 * t + tr;
                 boff[t] = kOOB;
                 orow[t] = -1;
                 bslot[t] = 0;
@@ -1728,13 +1729,13 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
                         __builtin_amdgcn_s_sleep(1);
                 }
             }
-            floatx4 acc[2][2][4];
+            floatx4 acc[2][2][TPW];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[s][h][t] = (floatx4)0.0f;
+                    for (int t = 0; t < TPW; ++t) acc[s][h][t] = (floatx4)0.0f;
             // B fragments of half kh of step sc: tile t, fragment kg (columns
             // kh*512 + kg*128 + 32*dw + [0, 32) of chunk sc >> 2; lane (tok, kq): 8 of them)
             auto kvalid = [&](int sc, int kh, int kg) { return (sc >> 2) * 1024 + kh * 512 + kg * 128 < it.klen; };
@@ -1742,10 +1743,10 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
             // memory), so the loads in flight are the same on every path and the
             // waits before the MFMAs count exactly: a conditional prefetch would
             // make them wait for it too.
-            auto load_b = [&](int sc, int kh, half8 (&bq)[4][4], bool on) {
+            auto load_b = [&](int sc, int kh, half8 (&bq)[TPW][4], bool on) {
                 const int col = (sc >> 2) * 1024 + kh * 512 + (sc & 3) * 32;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < TPW; ++t)
 #pragma unroll
                     for (int kg = 0; kg < 4; ++kg) {
                         // a select, not a branch: no short-circuit evaluation
@@ -1760,7 +1761,7 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
             // The fragments of k-block kg + 1 are read before the MFMAs of kg, so
             // the LDS latency overlaps the matrix work. Fragments past K are never
             // multiplied (their B fragments are zero anyway).
-            auto mma = [&](int sc, int kh, const half8 (&bq)[4][4]) {
+            auto mma = [&](int sc, int kh, const half8 (&bq)[TPW][4]) {
                 if (ntl == 0) return;
                 const unsigned char* wb = wbuf + (sc & 1) * kWStepBytes + lane * 16;
                 half8 a[2][2][2];
@@ -1783,11 +1784,11 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
+                            for (int t = 0; t < TPW; ++t)
                                 acc[s][h][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[kg & 1][s][h], bq[t][kg], acc[s][h][t], 0, 0, 0);
                 }
             };
-            half8 bq0[4][4], bq1[4][4];
+            half8 bq0[TPW][4], bq1[TPW][4];
             load_b(0, 0, bq0, true);
 #pragma unroll 1
             for (int sc = 0; sc < S; ++sc) {
@@ -1800,7 +1801,7 @@ __global__ __launch_bounds__(kBigWaves * 64, 1) void expert_kernel_big(ExpertPar
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
+                        for (int t = 0; t < TPW; ++t) {
                             if (t >= ntl || orow[t] < 0) continue;
                             const int row = h * 16 + kq * 4;   // rows row .. row+3 of the set
                             if (it.mode == 0) {

@@ -305,7 +305,7 @@ pw_status pw_debug_set_wait_limit(pw_layer layer, uint32_t polls);
  *                 expert on average, else the one-tile kernel (16-token
  *                 groups); 33..128 (33..64 when T >= 512): the four-tile
  *                 kernel (64-token groups); more: the dequantise-once kernel
- *                 (256-token groups)
+ *                 (128-token groups)
  *   PW_PATH_SMALL every expert in the one-tile kernel (16-token groups)
  *   PW_PATH_FOUR  as PW_PATH_AUTO up to 32 tokens; more: the four-tile kernel
  *                 (64-token groups, every weight dequantised once per group)

@@ -150,7 +150,7 @@ def test_expert_paths(torch_dev, name, T):
     """Every A/B path of the expert kernels on the same layer and batch: the one-tile kernel alone,
     the two-tile kernel alone (32-token groups, ragged last groups), the four-tile kernel for
     experts above 32 tokens, the dequantise-once kernel for them (the default) and for every
-    expert. T = 300 puts the qwen shared expert in two 256-token passes (a ragged 44-token second
+    expert. T = 300 puts the qwen shared expert in three 128-token passes (a ragged 44-token third
     pass); tiny_d256 and fine_e128_t128 have routed experts above 32 tokens."""
     cfg = synth.CONFIGS[name].with_tokens(T)
     _say(f"{name} T={T}: expert paths")
@@ -176,7 +176,7 @@ def test_expert_paths(torch_dev, name, T):
 def test_deterministic_accumulation(torch_dev, name, T):
     """PW_FLAG_DETERMINISTIC: two forwards of the same batch give bit-identical y on every expert
     path, and each matches the oracle. qwen T = 300 runs the two-tile kernel (routed experts, T k
-    above 16 per expert) and the dequantise-once kernel (the shared expert in two passes, three
+    above 16 per expert) and the dequantise-once kernel (the shared expert in three passes, three
     K-pieces); mixtral T = 64 runs the one- and four-tile kernels with seven K-pieces per routed
     down projection; the two path runs both layers in the two-tile kernel."""
     torch, dev = torch_dev
