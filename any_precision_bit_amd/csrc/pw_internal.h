@@ -171,10 +171,11 @@ constexpr int kBigTokens = 128;           // dequantise-once kernel: groups of 1
 // Experts with 33..kFourMax tokens go to the four-tile kernel (one or two
 // 64-token groups). The dequantise-once kernel has the higher cost per item and
 // pays off once a forward brings it many items: from kBigBatch tokens on, the
-// bound drops to kFourMaxBig (measured crossover on the qwen and fine-grained
-// layers at T = 128 and T = 1024).
+// bound drops to kFourMaxBig = kSmallMax, so every expert above 32 tokens takes
+// the dequantise-once kernel and the four-tile kernel is not launched (measured
+// crossover on the qwen and fine-grained layers at T = 128 and T = 1024).
 constexpr int kFourMax = 128;
-constexpr int kFourMaxBig = 64;
+constexpr int kFourMaxBig = 32;
 constexpr int kBigBatch = 512;
 // Which kernel takes which experts (PW_FORCE_PATH, pw_debug_set_path):
 //   AUTO  1..kSmallMax tokens: two-tile kernel when T k > 16 E, else one-tile kernel;

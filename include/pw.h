@@ -303,7 +303,7 @@ pw_status pw_debug_set_wait_limit(pw_layer layer, uint32_t polls);
  *   PW_PATH_AUTO  experts with 1..32 tokens: the two-tile kernel (one 32-token
  *                 group) when the T*top_k assignments exceed 16 per routed
  *                 expert on average, else the one-tile kernel (16-token
- *                 groups); 33..128 (33..64 when T >= 512): the four-tile
+ *                 groups); 33..128 (none when T >= 512): the four-tile
  *                 kernel (64-token groups); more: the dequantise-once kernel
  *                 (128-token groups)
  *   PW_PATH_SMALL every expert in the one-tile kernel (16-token groups)
