@@ -228,3 +228,22 @@ def test_row_block_validation(B):
         assert ei.value.status == 4                                                # others unbound
     finally:
         B.pw_layer_destroy(h)
+
+
+def test_path_hook(B):
+    """pw_debug_set_path takes the five declared paths by name or number and rejects the rest."""
+    with pytest.raises(B.PwError) as ei:
+        B.pw_debug_set_path(0, "auto")                # null layer
+    assert ei.value.status == 1
+    h = B.pw_layer_create(256, 8, 512, 2, 0, 16)
+    try:
+        for name, num in B.PATHS.items():
+            B.pw_debug_set_path(h, name)
+            B.pw_debug_set_path(h, num)
+        assert sorted(B.PATHS.values()) == [0, 1, 2, 3, 4]
+        for bad in (-1, 5):
+            with pytest.raises(B.PwError) as ei:
+                B.pw_debug_set_path(h, bad)
+            assert ei.value.status == 1
+    finally:
+        B.pw_layer_destroy(h)
